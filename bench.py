@@ -1,0 +1,185 @@
+"""Benchmark of the software-pipelined tiled GEMM on one MI355X.
+
+A step is one GEMM call, C = A[M,K] . B^T, on inputs already resident in
+HBM.  The headline workload is the 4096^3 fp16 NT GEMM; `value` is its
+throughput in TFLOP/s (2MNK / t).  The line also carries the num_stages sweep
+of the 128x128x32 tile (the pages' default) and of the headline tile, the
+roofline of the kernel (MFMA bound, measured with HIP events on the launch
+stream), and the CPU oracle timed on a bounded row sample of the same GEMM.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-cpu-baseline]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA, published
+HEADLINE = dict(workload="nt_f16_4096", block=(256, 256, 64), num_stages=2, threads=256)
+SWEEPS = [
+    # (label, workload, block, threads, stages)
+    ("tile128x128x32_t256", "nt_f16_4096", (128, 128, 32), 256, (1, 2, 3, 4, 6)),
+    ("tile256x256x32_t256", "nt_f16_4096", (256, 256, 32), 256, (1, 2, 3, 4)),
+    ("tile256x256x64_t256", "nt_f16_4096", (256, 256, 64), 256, (1, 2)),
+]
+
+
+def _log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def _device_inputs(w):
+    import numpy as np
+    import torch
+
+    from software_pipelined_tiled_03_amd import inputs
+
+    A, B = w.make()
+    tdt = torch.float16 if w.dtype == inputs.F16 else torch.bfloat16
+    dA = torch.from_numpy(A.view(np.int16)).cuda().view(tdt)
+    dB = torch.from_numpy(B.view(np.int16)).cuda().view(tdt)
+    return A, B, dA, dB
+
+
+def time_gemm(fn, dA, dB, C, block, stages, threads, steps, warmup):
+    """Average milliseconds per call over `steps` back-to-back launches."""
+    import torch
+
+    for _ in range(warmup):
+        fn(dA, dB, out=C, block=block, num_stages=stages, threads=threads)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        fn(dA, dB, out=C, block=block, num_stages=stages, threads=threads)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(w, A, B, rows):
+    """The CPU oracle (as it stands) on the first `rows` rows of C."""
+    from oracle import gemm as og
+
+    fn = og.gemm_nt if w.layout == "nt" else og.gemm_nn
+    fn(A, B, w.dtype, rows=(0, 1))  # load / warm
+    t0 = time.perf_counter()
+    fn(A, B, w.dtype, rows=(0, rows))
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * w.N * w.K
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=og.num_threads(), kind="oracle",
+                sample="rows 0..%d of C (%d x %d x %d, %s), %.1f GFLOP in %.2f s"
+                       % (rows - 1, w.M, w.N, w.K, w.layout.upper(), flops / 1e9, dt))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this GEMM runs on a single MI355X; "
+              "--gpus %d is not supported" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+
+    import software_pipelined_tiled_03_amd as pg
+    from software_pipelined_tiled_03_amd import inputs
+
+    if not torch.cuda.is_available():
+        print("no GPU available", file=sys.stderr)
+        return 1
+    pg.load()
+
+    w = inputs.workload(HEADLINE["workload"])
+    A, B, dA, dB = _device_inputs(w)
+    fn = pg.gemm_nt if w.layout == "nt" else pg.gemm_nn
+    C = torch.empty((w.M, w.N), dtype=dA.dtype, device="cuda")
+    flops = 2.0 * w.M * w.N * w.K
+
+    sweep = {}
+    if not args.no_sweep:
+        for label, wl, block, th, stages in SWEEPS:
+            assert wl == HEADLINE["workload"]
+            row = {}
+            for s in stages:
+                ms = time_gemm(fn, dA, dB, C, block, s, th, steps=30, warmup=5)
+                row[str(s)] = dict(tflops=round(flops / ms / 1e9, 1), pct_peak=round(100 * flops / ms / 1e9 / PEAK_TFLOPS, 1),
+                                   lds_bytes=pg.gemm_lds_bytes(block[0], block[1], block[2], s))
+                _log("sweep %s S=%d: %.1f TFLOP/s" % (label, s, flops / ms / 1e9))
+            rej = None
+            try:
+                fn(dA, dB, out=C, block=(256, 256, 64), num_stages=4, threads=256)
+            except pg.LdsBudgetError as e:
+                rej = str(e)
+            sweep[label] = row
+        sweep["rejected_256x256x64_S4"] = rej
+
+    block, stages, threads = HEADLINE["block"], HEADLINE["num_stages"], HEADLINE["threads"]
+    ms = time_gemm(fn, dA, dB, C, block, stages, threads, steps=args.steps, warmup=args.warmup)
+    tflops = flops / ms / 1e9
+    _log("headline %s tile %s S=%d threads=%d: %.3f ms, %.1f TFLOP/s" % (w.name, block, stages, threads, ms, tflops))
+
+    # context: the vendor library on the same operands
+    ref = None
+    try:
+        torch.matmul(dA, dB.t())
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(20):
+            torch.matmul(dA, dB.t())
+        t1.record()
+        torch.cuda.synchronize()
+        ref = round(flops / (t0.elapsed_time(t1) / 20) / 1e9, 1)
+    except Exception as e:  # context only
+        _log("torch.matmul context failed: %s" % e)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, A, B, min(args.cpu_rows, w.M))
+        _log("cpu oracle: %.4f TFLOP/s on %d threads" % (cpu["value"], cpu["cores"]))
+
+    out = {
+        "metric": "TFLOP/s (2MNK/t) and % of MFMA peak at 4096^3 fp16, per num_stages",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "strong",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "GEMM NT %dx%dx%d fp16 uniform[-1,1], fp32 accumulate" % (w.M, w.N, w.K),
+                   "M": w.M, "N": w.N, "K": w.K, "layout": "NT", "block": list(block),
+                   "num_stages": stages, "threads": threads},
+        "pct_peak": round(100 * tflops / PEAK_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_TFLOPS, 4), "traffic": None},
+        "cpu_baseline": cpu,
+        "per_num_stages": sweep,
+        "context_torch_matmul_tflops": ref,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,144 @@
+/*
+ * pipegemm — a software-pipelined tiled half-precision GEMM for MI355X (gfx950).
+ *
+ *   C[M,N] = A[M,K] x B          fp16 or bf16 inputs, fp32 accumulation,
+ *                                C written in the input dtype (round to
+ *                                nearest, ties to even)
+ *
+ * Two storage forms of B:
+ *   gemm_nt  B stored [N,K] row-major (the transpose_B form of the TileLang
+ *            tutorial, chapter 11 "pipeline and autotuning", sections 1.1/3.5:
+ *            the kernel signature takes A (M,K), B (N,K), C (M,N)).
+ *   gemm_nn  B stored [K,N] row-major (the plain form C = A @ B of the
+ *            "Stage 04 - GEMM" notes, "concepts" and "code").
+ *
+ * Each workgroup owns a block_M x block_N tile of C and walks the K dimension
+ * in block_K steps.  The tiles of A and B it needs are copied from HBM into a
+ * ring of num_stages LDS buffers; copies for later K steps are in flight while
+ * the matrix cores work on the current one (chapter 11, sections 1.1-1.3 and
+ * 2.3: multi-buffering lets the copy of round ko+1 overlap the compute of round
+ * ko; section 4.3: prologue, steady state, epilogue).
+ *
+ * Shared conventions for every entry point below:
+ *  - All sizes are in elements; all matrices are dense, row-major, with no
+ *    padding (leading dimension = number of columns).
+ *  - A, B and C are DEVICE pointers owned by the caller.  The library never
+ *    allocates, frees, or retains them, and keeps no state except a per-device
+ *    cache of the LDS limit and a per-thread error message.
+ *  - Calls that launch work are asynchronous on the caller's HIP stream
+ *    (hip_stream is a hipStream_t; NULL means the null stream).  They return
+ *    once the kernel is enqueued.
+ *  - Validation is synchronous and happens before any launch.  On any status
+ *    other than GEMM_OK nothing is launched and C is not touched;
+ *    gemm_last_error() then describes the failure.
+ *  - Validation order: (1) arguments, (2) LDS budget, (3) alignment,
+ *    (4) supported configuration.  An over-budget request therefore always
+ *    reports GEMM_ERR_LDS_BUDGET, whatever else is wrong with its tile.
+ */
+#ifndef PIPEGEMM_H
+#define PIPEGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum gemm_dtype {
+    GEMM_F16 = 0,  /* IEEE binary16 */
+    GEMM_BF16 = 1  /* bfloat16 */
+};
+
+enum gemm_layout {
+    GEMM_NT = 0, /* B stored [N,K] */
+    GEMM_NN = 1  /* B stored [K,N] */
+};
+
+enum gemm_status {
+    GEMM_OK = 0,
+    GEMM_ERR_ARG = 1,         /* negative size, null pointer, unknown dtype/layout, bad block/stage/thread value */
+    GEMM_ERR_LDS_BUDGET = 2,  /* num_stages x (block_M + block_N) x block_K x 2 bytes exceeds the LDS limit */
+    GEMM_ERR_UNSUPPORTED = 3, /* no kernel is built for this (dtype, layout, tile, threads) or size limits exceeded */
+    GEMM_ERR_ALIGN = 4,       /* K (and N for NN) not a multiple of 8, or misaligned pointers */
+    GEMM_ERR_HIP = 5          /* a HIP runtime call failed (no device, launch failure) */
+};
+
+/*
+ * gemm_nt: C[M,N] = A[M,K] . B[N,K]^T.
+ *
+ * Defined by: TileLang tutorial, chapter 11, section 1.1 (the tiled loop with
+ * transpose_B) and section 3.5 (the kernel signature and its parameters with
+ * defaults block 128x128x32, num_stages 3, threads 128, fp16 in, fp32
+ * accumulate); section 2.1 / 5.4 for num_stages = 0.
+ *
+ * Arguments:
+ *   A           device pointer, [M,K] row-major, dtype elements, 16-byte aligned
+ *   B           device pointer, [N,K] row-major, 16-byte aligned
+ *   C           device pointer, [M,N] row-major, written in dtype, 8-byte aligned
+ *   M, N, K     sizes, >= 0.  M == 0 or N == 0 is a no-op; K == 0 writes C = 0.
+ *               K must be a multiple of 8.
+ *   dtype       GEMM_F16 or GEMM_BF16 (A, B and C share it)
+ *   block_M/N/K the C tile one workgroup owns and the K step (elements)
+ *   num_stages  number of LDS ring buffers; 1 = single buffer, no overlap
+ *               (the non-pipelined control); 0 = alias of 1 (a loop that is not
+ *               pipelined is single-buffered)
+ *   threads     threads per workgroup, a multiple of 64 (0 selects 256)
+ *   hip_stream  hipStream_t to launch on, or NULL
+ * Returns a gemm_status.  Partial tiles at the M, N and K edges are handled:
+ * out-of-range A/B elements are read as zero and out-of-range C is never written.
+ */
+int gemm_nt(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype,
+            int block_M, int block_N, int block_K, int num_stages, int threads, void *hip_stream);
+
+/*
+ * gemm_nn: C[M,N] = A[M,K] . B[K,N].
+ *
+ * Defined by: "Stage 04 - GEMM" notes ("concepts": C[M,N] = A[M,K] @ B[K,N],
+ * fp32 accumulation; "code": T.gemm(A_shared, B_shared, C_local) inside a
+ * T.Pipelined K loop).  Arguments and behaviour as gemm_nt, except B is
+ * [K,N] row-major and N must also be a multiple of 8.
+ */
+int gemm_nn(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype,
+            int block_M, int block_N, int block_K, int num_stages, int threads, void *hip_stream);
+
+/*
+ * gemm_lds_bytes: LDS the pipeline of one workgroup needs,
+ *   max(num_stages, 1) x (block_M x block_K + block_K x block_N) x 2 bytes.
+ *
+ * Defined by: TileLang tutorial, chapter 11, section 4.5 (per-stage bytes of
+ * the A and B tiles times the stage count; the accumulator lives in registers).
+ * Pure host arithmetic.  Returns -1 for a negative block size, a negative stage
+ * count or an unknown dtype.
+ */
+int64_t gemm_lds_bytes(int block_M, int block_N, int block_K, int num_stages, int dtype);
+
+/*
+ * gemm_lds_budget: the LDS limit of one workgroup on the current HIP device
+ * (hipDeviceAttributeMaxSharedMemoryPerBlock; 163840 bytes on gfx950).
+ * Returns -1 if no device is available (see gemm_last_error()).
+ */
+int64_t gemm_lds_budget(void);
+
+/*
+ * gemm_check: run the validation of gemm_nt / gemm_nn (layout selects which)
+ * on sizes and configuration alone, against the given LDS budget in bytes
+ * (0 = the current device's, which needs a device).  Pointer checks are
+ * skipped.  Pure host code when lds_budget > 0: no device is touched.
+ * Defined by: chapter 11, sections 4.5 and 5.1 (over budget is a hard
+ * failure, never a slowdown).  Returns a gemm_status.
+ */
+int gemm_check(int layout, int64_t M, int64_t N, int64_t K, int dtype, int block_M, int block_N,
+               int block_K, int num_stages, int threads, int64_t lds_budget);
+
+/*
+ * gemm_last_error: message describing the last non-OK status returned on
+ * this thread ("" if none).  The string is owned by the library and stays
+ * valid until the next call on this thread.
+ */
+const char *gemm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PIPEGEMM_H */

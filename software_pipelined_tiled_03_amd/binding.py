@@ -1,0 +1,179 @@
+"""Python binding of the C-ABI library declared in include/pipegemm.h.
+
+Argument marshalling only: every step of the GEMM runs in the library's HIP
+kernels.  torch supplies device memory and the current stream.  The library
+must have been built (software_pipelined_tiled_03_amd/build.py); if it is
+missing, every call raises -- there is no fallback path.
+"""
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libpipegemm.so")
+
+GEMM_F16 = 0
+GEMM_BF16 = 1
+GEMM_NT = 0
+GEMM_NN = 1
+
+GEMM_OK = 0
+GEMM_ERR_ARG = 1
+GEMM_ERR_LDS_BUDGET = 2
+GEMM_ERR_UNSUPPORTED = 3
+GEMM_ERR_ALIGN = 4
+GEMM_ERR_HIP = 5
+
+STATUS_NAMES = {GEMM_OK: "GEMM_OK", GEMM_ERR_ARG: "GEMM_ERR_ARG", GEMM_ERR_LDS_BUDGET: "GEMM_ERR_LDS_BUDGET",
+                GEMM_ERR_UNSUPPORTED: "GEMM_ERR_UNSUPPORTED", GEMM_ERR_ALIGN: "GEMM_ERR_ALIGN",
+                GEMM_ERR_HIP: "GEMM_ERR_HIP"}
+
+
+class GemmError(Exception):
+    """Base class; .status holds the gemm_status code."""
+
+    def __init__(self, status, message):
+        super().__init__("%s: %s" % (STATUS_NAMES.get(status, status), message))
+        self.status = status
+
+
+class GemmArgumentError(GemmError, ValueError):
+    pass
+
+
+class LdsBudgetError(GemmError, ValueError):
+    """num_stages x (block_M + block_N) x block_K x 2 bytes exceeds the LDS limit."""
+
+
+class UnsupportedConfigError(GemmError, ValueError):
+    pass
+
+
+class AlignmentError(GemmError, ValueError):
+    pass
+
+
+class GemmHipError(GemmError, RuntimeError):
+    pass
+
+
+_EXC = {GEMM_ERR_ARG: GemmArgumentError, GEMM_ERR_LDS_BUDGET: LdsBudgetError,
+        GEMM_ERR_UNSUPPORTED: UnsupportedConfigError, GEMM_ERR_ALIGN: AlignmentError, GEMM_ERR_HIP: GemmHipError}
+
+_lib = None
+
+
+def load():
+    """Load the C-ABI library (once) and declare its signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("pipegemm library not built: %s is missing "
+                           "(run `python software_pipelined_tiled_03_amd/build.py`)" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    for name in ("gemm_nt", "gemm_nn"):
+        f = getattr(lib, name)
+        f.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, vp]
+        f.restype = i32
+    lib.gemm_lds_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.gemm_lds_bytes.restype = i64
+    lib.gemm_lds_budget.argtypes = []
+    lib.gemm_lds_budget.restype = i64
+    lib.gemm_check.argtypes = [i32, i64, i64, i64, i32, i32, i32, i32, i32, i32, i64]
+    lib.gemm_check.restype = i32
+    lib.gemm_last_error.argtypes = []
+    lib.gemm_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().gemm_last_error().decode()
+
+
+def _raise_for(status):
+    if status != GEMM_OK:
+        raise _EXC.get(status, GemmError)(status, last_error())
+
+
+# --- raw C-ABI mirrors (same names and arguments as the header) -------------
+
+def gemm_nt_raw(A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, threads, hip_stream):
+    """gemm_nt on raw device addresses; returns the status code."""
+    return load().gemm_nt(A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, threads, hip_stream)
+
+
+def gemm_nn_raw(A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, threads, hip_stream):
+    """gemm_nn on raw device addresses; returns the status code."""
+    return load().gemm_nn(A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, threads, hip_stream)
+
+
+def gemm_lds_bytes(block_M, block_N, block_K, num_stages, dtype=GEMM_F16) -> int:
+    return int(load().gemm_lds_bytes(block_M, block_N, block_K, num_stages, dtype))
+
+
+def gemm_lds_budget() -> int:
+    v = int(load().gemm_lds_budget())
+    if v < 0:
+        raise GemmHipError(GEMM_ERR_HIP, last_error())
+    return v
+
+
+def gemm_check(layout, M, N, K, dtype, block_M, block_N, block_K, num_stages, threads, lds_budget) -> int:
+    """Validation only (status code); lds_budget > 0 touches no device."""
+    return int(load().gemm_check(layout, M, N, K, dtype, block_M, block_N, block_K, num_stages, threads,
+                                 lds_budget))
+
+
+# --- torch convenience wrappers --------------------------------------------
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float16:
+        return GEMM_F16
+    if t.dtype == torch.bfloat16:
+        return GEMM_BF16
+    raise GemmArgumentError(GEMM_ERR_ARG, "dtype must be float16 or bfloat16, got %s" % t.dtype)
+
+
+def _gemm(layout, A, B, out, block, num_stages, threads, stream):
+    import torch
+    if A.dim() != 2 or B.dim() != 2:
+        raise GemmArgumentError(GEMM_ERR_ARG, "A and B must be 2-D")
+    if not (A.is_cuda and B.is_cuda):
+        raise GemmArgumentError(GEMM_ERR_ARG, "A and B must be device tensors")
+    if not (A.is_contiguous() and B.is_contiguous()):
+        raise GemmArgumentError(GEMM_ERR_ARG, "A and B must be contiguous row-major")
+    if A.dtype != B.dtype:
+        raise GemmArgumentError(GEMM_ERR_ARG, "A and B dtypes differ")
+    M, K = A.shape
+    if layout == GEMM_NT:
+        N, Kb = B.shape
+    else:
+        Kb, N = B.shape
+    if Kb != K:
+        raise GemmArgumentError(GEMM_ERR_ARG, "inner dimensions differ: %d vs %d" % (K, Kb))
+    if out is None:
+        out = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    elif (out.shape != (M, N) or out.dtype != A.dtype or not out.is_contiguous() or out.device != A.device):
+        raise GemmArgumentError(GEMM_ERR_ARG, "out must be a contiguous (M, N) tensor of A's dtype and device")
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+    bm, bn, bk = block
+    fn = load().gemm_nt if layout == GEMM_NT else load().gemm_nn
+    with torch.cuda.device(A.device):
+        st = fn(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K, _dtype_code(A), bm, bn, bk, num_stages,
+                threads, stream)
+    _raise_for(st)
+    return out
+
+
+def gemm_nt(A, B, out=None, block=(128, 128, 32), num_stages=3, threads=256, stream=None):
+    """C = A[M,K] @ B[N,K]^T on the GPU (fp16/bf16 in, fp32 accumulate, C in A's dtype)."""
+    return _gemm(GEMM_NT, A, B, out, block, num_stages, threads, stream)
+
+
+def gemm_nn(A, B, out=None, block=(128, 128, 32), num_stages=3, threads=256, stream=None):
+    """C = A[M,K] @ B[K,N] on the GPU (fp16/bf16 in, fp32 accumulate, C in A's dtype)."""
+    return _gemm(GEMM_NN, A, B, out, block, num_stages, threads, stream)

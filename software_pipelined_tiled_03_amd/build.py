@@ -1,0 +1,83 @@
+"""Build the HIP library (software_pipelined_tiled_03_amd/_lib/libpipegemm.so) for gfx950.
+
+The library is plain C-ABI (include/pipegemm.h); it is built in-tree with hipcc
+so that it travels with the source tree.
+"""
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+LIBDIR = os.path.join(PKG, "_lib")
+LIB = os.path.join(LIBDIR, "libpipegemm.so")
+KERNEL_SRC = os.path.join(CSRC, "pipegemm_kernels.hip")
+HOST_SRC = os.path.join(CSRC, "pipegemm.hip")
+DEPS = [KERNEL_SRC, HOST_SRC, os.path.join(CSRC, "pipegemm_kernel.hpp"), os.path.join(CSRC, "pipegemm_launch.hpp"),
+        os.path.join(ROOT, "include", "pipegemm.h")]
+# one kernel translation unit per (element type, B layout), compiled in parallel
+VARIANTS = [("f16_nt", "_Float16", 0), ("bf16_nt", "__bf16", 0), ("f16_nn", "_Float16", 1), ("bf16_nn", "__bf16", 1)]
+
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    # no packed-fp32 VALU instructions in device code
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-result",
+    "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
+]
+
+
+def _compile_cmds(objdir, extra):
+    cmds = []
+    for name, elem, nn in VARIANTS:
+        obj = os.path.join(objdir, "kernels_%s.o" % name)
+        cmds.append((obj, [HIPCC, *FLAGS, *extra, "-DPG_ELEM=" + elem, "-DPG_NN=%d" % nn, "-c", KERNEL_SRC,
+                           "-o", obj]))
+    obj = os.path.join(objdir, "host.o")
+    cmds.append((obj, [HIPCC, *FLAGS, *extra, "-c", HOST_SRC, "-o", obj]))
+    return cmds
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    """Compile the library (always) and return its path."""
+    import tempfile
+    from concurrent.futures import ThreadPoolExecutor
+
+    os.makedirs(LIBDIR, exist_ok=True)
+    with tempfile.TemporaryDirectory(prefix="pipegemm_build_") as objdir:
+        cmds = _compile_cmds(objdir, list(extra))
+        workers = max(1, min(len(cmds), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+
+        def run(c):
+            if verbose:
+                print(" ".join(c[1]), flush=True)
+            return subprocess.run(c[1], capture_output=True, text=True)
+
+        with ThreadPoolExecutor(workers) as ex:
+            results = list(ex.map(run, cmds))
+        for (obj, cmd), r in zip(cmds, results):
+            err = "\n".join(ln for ln in r.stderr.splitlines() if "packed-fp32-ops" not in ln)
+            if r.returncode != 0:
+                raise RuntimeError("build failed: %s\n%s" % (" ".join(cmd), err))
+            if verbose and err.strip():
+                print(err, file=sys.stderr)
+        tmp = LIB + ".tmp"
+        link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *[o for o, _ in cmds], "-o", tmp]
+        if verbose:
+            print(" ".join(link), flush=True)
+        subprocess.run(link, check=True)
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def is_stale() -> bool:
+    if not os.path.exists(LIB):
+        return True
+    t = os.path.getmtime(LIB)
+    return any(os.path.getmtime(p) > t for p in DEPS)
+
+
+if __name__ == "__main__":
+    build(verbose=True)

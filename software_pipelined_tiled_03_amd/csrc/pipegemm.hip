@@ -1,0 +1,268 @@
+// Host side of the pipelined tiled GEMM: validation, the table of built
+// kernels, and the C-ABI entry points declared in include/pipegemm.h.
+#include "pipegemm.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <mutex>
+
+#include "pipegemm_kernel.hpp"
+#include "pipegemm_launch.hpp"
+
+namespace pipegemm {
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int ok()
+{
+    g_err[0] = '\0';
+    return GEMM_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Built kernels.  S is a run-time argument of every kernel; the table lists the
+// compile-time tile shapes (PG_TILE_LIST) for each dtype and B layout.
+typedef hipError_t (*launch_fn)(const KernelArgs &, int grid, int lds_bytes, hipStream_t);
+
+struct Instance {
+    int dtype, layout, bm, bn, bk, threads;
+    int loads_per_wave;  // 1 KiB copies per wave per K tile (bounds the vmcnt wait)
+    launch_fn launch;
+};
+
+#define PG_ROW(DT, T, LAYOUT, NN, BM, BN, BK, WM, WN) \
+    {DT, LAYOUT, BM, BN, BK, 64 * WM * WN, loads_per_wave(BM, BN, BK, WM * WN), &launch<T, NN, BM, BN, BK, WM, WN>},
+#define PG_ROW_F16_NT(BM, BN, BK, WM, WN) PG_ROW(GEMM_F16, _Float16, GEMM_NT, false, BM, BN, BK, WM, WN)
+#define PG_ROW_BF16_NT(BM, BN, BK, WM, WN) PG_ROW(GEMM_BF16, __bf16, GEMM_NT, false, BM, BN, BK, WM, WN)
+#define PG_ROW_F16_NN(BM, BN, BK, WM, WN) PG_ROW(GEMM_F16, _Float16, GEMM_NN, true, BM, BN, BK, WM, WN)
+#define PG_ROW_BF16_NN(BM, BN, BK, WM, WN) PG_ROW(GEMM_BF16, __bf16, GEMM_NN, true, BM, BN, BK, WM, WN)
+
+const Instance kInstances[] = {
+    PG_TILE_LIST(PG_ROW_F16_NT) PG_TILE_LIST(PG_ROW_BF16_NT)
+    PG_TILE_LIST(PG_ROW_F16_NN) PG_TILE_LIST(PG_ROW_BF16_NN)
+};
+
+const Instance *find_instance(int dtype, int layout, int bm, int bn, int bk, int threads)
+{
+    for (const Instance &in : kInstances)
+        if (in.dtype == dtype && in.layout == layout && in.bm == bm && in.bn == bn && in.bk == bk &&
+            in.threads == threads)
+            return &in;
+    return nullptr;
+}
+
+constexpr int kDefaultThreads = 256;
+
+int64_t lds_bytes_of(int bm, int bn, int bk, int stages)
+{
+    const int64_t s = stages < 1 ? 1 : stages;
+    return s * ((int64_t)bm * bk + (int64_t)bk * bn) * 2;
+}
+
+// The checks shared by gemm_check and the launching entry points, in the
+// documented order: arguments, LDS budget, alignment (sizes only), supported
+// configuration.  On success *inst receives the kernel to launch.
+// ptrs is null for a size-only check; otherwise it holds A, B, C.
+int validate(int layout, int64_t M, int64_t N, int64_t K, int dtype, int bm, int bn, int bk, int stages,
+             int threads, int64_t budget, const void *const *ptrs, const Instance **inst)
+{
+    // (1) arguments
+    if (layout != GEMM_NT && layout != GEMM_NN)
+        return fail(GEMM_ERR_ARG, "unknown layout %d", layout);
+    if (M < 0 || N < 0 || K < 0)
+        return fail(GEMM_ERR_ARG, "negative size M=%lld N=%lld K=%lld", (long long)M, (long long)N,
+                    (long long)K);
+    if (dtype != GEMM_F16 && dtype != GEMM_BF16)
+        return fail(GEMM_ERR_ARG, "unknown dtype %d", dtype);
+    if (bm <= 0 || bn <= 0 || bk <= 0)
+        return fail(GEMM_ERR_ARG, "block sizes must be positive (got %d x %d x %d)", bm, bn, bk);
+    if (stages < 0)
+        return fail(GEMM_ERR_ARG, "num_stages must be >= 0 (got %d)", stages);
+    if (threads < 0 || threads % 64 != 0 || threads > 1024)
+        return fail(GEMM_ERR_ARG, "threads must be 0 or a multiple of 64 up to 1024 (got %d)", threads);
+    if (ptrs && M > 0 && N > 0) {
+        if (!ptrs[2])
+            return fail(GEMM_ERR_ARG, "C is null");
+        if (K > 0 && (!ptrs[0] || !ptrs[1]))
+            return fail(GEMM_ERR_ARG, "A or B is null");
+    }
+    if (budget <= 0)
+        return fail(GEMM_ERR_ARG, "LDS budget must be positive");
+    // (2) LDS budget: num_stages x (A tile + B tile), checked before anything else about the tile
+    const int64_t need = lds_bytes_of(bm, bn, bk, stages);
+    if (need > budget)
+        return fail(GEMM_ERR_LDS_BUDGET,
+                    "LDS budget exceeded: %d stage(s) x (%d x %d + %d x %d) x 2 B = %lld B > %lld B available",
+                    stages < 1 ? 1 : stages, bm, bk, bk, bn, (long long)need, (long long)budget);
+    // (3) alignment: 16-byte copies along the contiguous dimension of A and B
+    if (K % 8 != 0)
+        return fail(GEMM_ERR_ALIGN, "K must be a multiple of 8 (got %lld)", (long long)K);
+    if (layout == GEMM_NN && N % 8 != 0)
+        return fail(GEMM_ERR_ALIGN, "N must be a multiple of 8 for the NN form (got %lld)", (long long)N);
+    if (ptrs && ((((uintptr_t)ptrs[0]) & 15) || (((uintptr_t)ptrs[1]) & 15)))
+        return fail(GEMM_ERR_ALIGN, "A and B must be 16-byte aligned");
+    if (ptrs && (((uintptr_t)ptrs[2]) & 7))
+        return fail(GEMM_ERR_ALIGN, "C must be 8-byte aligned");
+    // (4) supported configuration and size limits of the kernels' 32-bit offsets
+    const int th = threads == 0 ? kDefaultThreads : threads;
+    const Instance *in = find_instance(dtype, layout, bm, bn, bk, th);
+    if (!in)
+        return fail(GEMM_ERR_UNSUPPORTED,
+                    "no kernel built for %s %s tile %dx%dx%d with %d threads", dtype == GEMM_F16 ? "fp16" : "bf16",
+                    layout == GEMM_NT ? "NT" : "NN", bm, bn, bk, th);
+    const int s = stages < 1 ? 1 : stages;
+    if (s > kMaxStages)
+        return fail(GEMM_ERR_UNSUPPORTED, "num_stages above %d is not supported", kMaxStages);
+    if (s >= 2 && (int64_t)in->loads_per_wave * (s - 2) > 63)
+        return fail(GEMM_ERR_UNSUPPORTED,
+                    "%d stages x %d copies per wave exceed the 63 loads one wave can keep in flight", s,
+                    in->loads_per_wave);
+    const int64_t lim = (int64_t)1 << 31;
+    if (M >= lim || N >= lim || K >= lim)
+        return fail(GEMM_ERR_UNSUPPORTED, "sizes must be below 2^31");
+    const int64_t panel = (int64_t)(bm > bn ? bm : bn) * K * 2;
+    if (panel >= lim)
+        return fail(GEMM_ERR_UNSUPPORTED, "a %lld-byte operand panel exceeds the 2 GiB addressable per workgroup",
+                    (long long)panel);
+    if (layout == GEMM_NN && K * N * 2 >= lim)
+        return fail(GEMM_ERR_UNSUPPORTED, "B of the NN form must be below 2 GiB");
+    if (inst)
+        *inst = in;
+    return ok();
+}
+
+// LDS limit of a device, cached.
+std::atomic<int64_t> g_budget[64];
+
+int device_budget(int64_t *out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return fail(GEMM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev >= 0 && dev < 64) {
+        const int64_t c = g_budget[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *out = c;
+            return GEMM_OK;
+        }
+    }
+    int v = 0;
+    e = hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+    if (e != hipSuccess)
+        return fail(GEMM_ERR_HIP, "hipDeviceGetAttribute: %s", hipGetErrorString(e));
+    if (dev >= 0 && dev < 64)
+        g_budget[dev].store(v, std::memory_order_relaxed);
+    *out = v;
+    return GEMM_OK;
+}
+
+int run(int layout, const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype, int bm,
+        int bn, int bk, int stages, int threads, void *stream)
+{
+    const void *ptrs[3] = {A, B, C};
+    // Argument errors are reported as such even when no device can be queried:
+    // run the checks once against an unlimited budget first.
+    int st = validate(layout, M, N, K, dtype, bm, bn, bk, stages, threads, 1LL << 40, ptrs, nullptr);
+    if (st == GEMM_ERR_ARG)
+        return st;
+    int64_t budget = 0;
+    st = device_budget(&budget);
+    if (st != GEMM_OK)
+        return st;
+    const Instance *in = nullptr;
+    st = validate(layout, M, N, K, dtype, bm, bn, bk, stages, threads, budget, ptrs, &in);
+    if (st != GEMM_OK)
+        return st;
+    if (M == 0 || N == 0)
+        return ok();
+
+    KernelArgs a;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.nk = (int)((K + bk - 1) / bk);
+    a.stages = stages < 1 ? 1 : stages;
+    a.tiles_m = (int)((M + bm - 1) / bm);
+    a.tiles_n = (int)((N + bn - 1) / bn);
+    a.group_m = a.tiles_m < 4 ? a.tiles_m : 4;
+    a.c_vec = (N % 4) == 0;
+    const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
+    if (grid >= (1LL << 31))
+        return fail(GEMM_ERR_UNSUPPORTED, "too many tiles");
+    const int lds = (int)lds_bytes_of(bm, bn, bk, a.stages);
+    hipError_t e = in->launch(a, (int)grid, lds, (hipStream_t)stream);
+    if (e != hipSuccess)
+        return fail(GEMM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+}  // namespace pipegemm
+
+extern "C" {
+
+int gemm_nt(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype, int block_M,
+            int block_N, int block_K, int num_stages, int threads, void *hip_stream)
+{
+    return pipegemm::run(GEMM_NT, A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, threads,
+                         hip_stream);
+}
+
+int gemm_nn(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype, int block_M,
+            int block_N, int block_K, int num_stages, int threads, void *hip_stream)
+{
+    return pipegemm::run(GEMM_NN, A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, threads,
+                         hip_stream);
+}
+
+int64_t gemm_lds_bytes(int block_M, int block_N, int block_K, int num_stages, int dtype)
+{
+    if (block_M < 0 || block_N < 0 || block_K < 0 || num_stages < 0 || (dtype != GEMM_F16 && dtype != GEMM_BF16))
+        return -1;
+    return pipegemm::lds_bytes_of(block_M, block_N, block_K, num_stages);
+}
+
+int64_t gemm_lds_budget(void)
+{
+    int64_t b = 0;
+    if (pipegemm::device_budget(&b) != GEMM_OK)
+        return -1;
+    return b;
+}
+
+int gemm_check(int layout, int64_t M, int64_t N, int64_t K, int dtype, int block_M, int block_N, int block_K,
+               int num_stages, int threads, int64_t lds_budget)
+{
+    int64_t budget = lds_budget;
+    if (budget == 0) {
+        const int st = pipegemm::device_budget(&budget);
+        if (st != GEMM_OK)
+            return st;
+    }
+    return pipegemm::validate(layout, M, N, K, dtype, block_M, block_N, block_K, num_stages, threads, budget,
+                              nullptr, nullptr);
+}
+
+const char *gemm_last_error(void)
+{
+    return pipegemm::g_err;
+}
+
+}  // extern "C"

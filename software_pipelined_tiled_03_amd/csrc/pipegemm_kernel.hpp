@@ -1,0 +1,440 @@
+// Device code of the software-pipelined tiled GEMM (gfx950 / MI355X).
+//
+// One workgroup owns a BM x BN tile of C.  Its K loop streams BM x BK tiles of
+// A and BN x BK (NT) or BK x BN (NN) tiles of B from HBM into a ring of S LDS
+// slots with direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds), and
+// feeds the matrix cores from the slot that has landed:
+//
+//   prologue      issue tiles 0 .. min(S-1, nk)-1 into slots 0 ..
+//   steady state  for kt:  wait until this wave's copies of tile kt landed
+//                          barrier   (every wave's copies of kt landed, and every
+//                                     wave finished computing kt-1, so slot
+//                                     (kt-1) mod S is free)
+//                          issue tile kt+S-1 into slot (kt+S-1) mod S
+//                          MFMA over slot kt mod S
+//   drain         the last S-1 iterations issue nothing
+//   S = 1         issue, wait, barrier, compute, barrier (two barriers per
+//                 round: copy and compute never overlap)
+//
+// This is the structure of the TileLang tutorial, chapter 11: section 1.1
+// (single buffer: every round costs copy + compute), section 2.3 (S versioned
+// buffers indexed by ko mod S), section 4.3 (prologue / body / epilogue with
+// max_stage = S - 1) and section 5.2 (write slot s only after its last reader
+// is done; read slot s only after its writer is done).
+//
+// Hardware mapping (gfx950):
+//  - copies: each wave issues 1 KiB direct-to-LDS loads (64 lanes x 16 B);
+//    lane i of a load lands at LDS base + 16 i, so the bank swizzle is applied
+//    by choosing which global 16-byte chunk each lane fetches;
+//  - the copy wait is s_waitcnt vmcnt(n), n = loads still allowed in flight
+//    (the copies of the tiles issued after kt); vmcnt counts in issue order;
+//  - compute: v_mfma_f32_32x32x16_{f16,bf16}, 16 fp32 accumulators per lane
+//    per 32x32 block, operands read from LDS with ds_read_b128 (k-contiguous
+//    tiles) or ds_read_b64_tr_b16 (the N-contiguous B tile of the NN form);
+//  - the MFMA is fed the B fragment as its first operand and the A fragment as
+//    its second, so it produces C^T blocks: each lane then holds 4 consecutive
+//    columns of one row of C and the epilogue stores 8 bytes at a time;
+//  - out-of-range rows and K/N chunks read as zero through the buffer
+//    resource's range check (an offset at or beyond num_records returns 0).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "pipegemm_layout.hpp"
+
+namespace pipegemm {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Kernel parameters, passed by value.
+struct KernelArgs {
+    const void *A;
+    const void *B;
+    void *C;
+    int M, N, K;
+    int nk;       // number of K tiles, ceil(K / BK)
+    int stages;   // LDS ring slots, >= 1
+    int tiles_m;  // ceil(M / BM)
+    int tiles_n;  // ceil(N / BN)
+    int group_m;  // tile rows swept before advancing along N (L2 reuse)
+    int c_vec;    // 1 when C rows allow 8-byte stores (N % 4 == 0)
+};
+
+// ---------------------------------------------------------------------------
+// Element types.
+template <class T>
+struct Elem;
+
+template <>
+struct Elem<_Float16> {
+    typedef f16x8 frag;
+    typedef f16x4 quad;
+    static __device__ __forceinline__ f32x16 mfma(frag a, frag b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <>
+struct Elem<__bf16> {
+    typedef bf16x8 frag;
+    typedef bf16x4 quad;
+    static __device__ __forceinline__ f32x16 mfma(frag a, frag b, f32x16 c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Tile geometry.  WM x WN waves; each wave owns a TM x TN sub-tile of C made
+// of FM x FN blocks of 32 x 32.
+template <int BM_, int BN_, int BK_, int WM_, int WN_>
+struct Tile {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+    static constexpr int WAVES = WM * WN;
+    static constexpr int THREADS = 64 * WAVES;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int FM = TM / 32, FN = TN / 32;
+    static constexpr int KSTEPS = BK / 16;             // MFMA k-steps per tile
+    static constexpr int A_BYTES = BM * BK * 2;
+    static constexpr int B_BYTES = BN * BK * 2;
+    static constexpr int SLOT_BYTES = A_BYTES + B_BYTES;
+    static constexpr int A_LOADS = A_BYTES / (1024 * WAVES);  // 1 KiB loads per wave per tile
+    static constexpr int B_LOADS = B_BYTES / (1024 * WAVES);
+    static constexpr int LOADS = A_LOADS + B_LOADS;
+    static_assert(BM % WM == 0 && BN % WN == 0, "waves must split the tile");
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave sub-tiles are made of 32x32 blocks");
+    static_assert(BK == 32 || BK == 64, "block_K must be 32 or 64");
+    static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0,
+                  "each wave must copy a whole number of 1 KiB pieces of each tile");
+    static_assert(LOADS >= 1, "at least one copy per wave");
+};
+
+// ---------------------------------------------------------------------------
+// Small device helpers.
+
+// s_waitcnt vmcnt(n) with every other counter left free (gfx9 encoding:
+// vmcnt[3:0] bits 3:0, vmcnt[5:4] bits 15:14, expcnt 6:4, lgkmcnt 11:8).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N <= 63, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Wait until at most `tiles` tiles' worth of this wave's copies are in flight.
+template <int LOADS>
+__device__ __forceinline__ void wait_tiles(int tiles)
+{
+    switch (tiles) {
+#define PG_WAIT_CASE(i) \
+    case i:             \
+        if constexpr (i * LOADS <= 63) wait_vmcnt<i * LOADS>(); else wait_vmcnt<0>(); \
+        break;
+        PG_WAIT_CASE(1) PG_WAIT_CASE(2) PG_WAIT_CASE(3) PG_WAIT_CASE(4)
+        PG_WAIT_CASE(5) PG_WAIT_CASE(6) PG_WAIT_CASE(7) PG_WAIT_CASE(8)
+#undef PG_WAIT_CASE
+    default:
+        wait_vmcnt<0>();
+        break;
+    }
+}
+
+// s_waitcnt lgkmcnt(0): every LDS read this wave issued has returned.
+__device__ __forceinline__ void wait_lds()
+{
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
+// Workgroup barrier.  Every LDS read this wave issued before it has returned
+// when it is passed (so a slot it read may be overwritten afterwards), and the
+// compiler may not move memory accesses across it.
+__device__ __forceinline__ void barrier()
+{
+    asm volatile("" ::: "memory");
+    wait_lds();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// One 16-byte-per-lane direct-to-LDS load: lane i's chunk lands at dst + 16 i.
+__device__ __forceinline__ void copy_1k(__amdgpu_buffer_rsrc_t rsrc, char *dst, uint32_t voffset)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void *)dst, 16, voffset, 0, 0, 0);
+}
+
+// An offset that is out of range for every buffer resource this kernel builds
+// (their num_records are all below 2^31), so the load returns zero.
+constexpr uint32_t kOOB = 0x80000000u;
+
+// Map the workgroup id to a C tile.  Workgroups are dispatched round-robin
+// over the 8 XCDs (id mod 8), each with its own L2: renumber so that the ids
+// one XCD receives are consecutive, then walk tiles in groups of group_m tile
+// rows so that the workgroups sharing an XCD share A panels and B panels.
+__device__ __forceinline__ void map_tile(const KernelArgs &p, int &tm, int &tn)
+{
+    const int nwg = p.tiles_m * p.tiles_n;
+    const int bid = blockIdx.x;
+    const int xcd = bid & 7, idx = bid >> 3;
+    const int per = nwg >> 3, rem = nwg & 7;
+    const int id = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    const int width = p.group_m * p.tiles_n;
+    const int first_m = (id / width) * p.group_m;
+    const int gsize = min(p.tiles_m - first_m, p.group_m);
+    const int in_group = id % width;
+    tm = first_m + in_group % gsize;
+    tn = in_group / gsize;
+}
+
+// ---------------------------------------------------------------------------
+// NN form: MFMA operand from the N-contiguous B tile, two transposed reads
+// (see nn_tr_offset for the lane mapping).
+template <class T, class Cfg>
+__device__ __forceinline__ typename Elem<T>::frag load_b_nn(const char *slot, int kk, int ncol0, int lane)
+{
+    i16x8 out;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const char *addr = slot + Cfg::A_BYTES + nn_tr_offset<Cfg::BN>(lane, kk, ncol0, h);
+        const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4 *)(addr));
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            out[4 * h + e] = v[e];
+    }
+    return __builtin_bit_cast(typename Elem<T>::frag, out);
+}
+
+// ---------------------------------------------------------------------------
+// The kernel.
+template <class T, bool NN, class Cfg>
+__global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs p)
+{
+    using E = Elem<T>;
+    using frag = typename E::frag;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
+    constexpr int WAVES = Cfg::WAVES, FM = Cfg::FM, FN = Cfg::FN;
+
+    extern __shared__ __attribute__((aligned(1024))) char smem[];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int wm = wave % Cfg::WM, wn = wave / Cfg::WM;
+
+    int tm, tn;
+    map_tile(p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int K = p.K, N = p.N, nk = p.nk;
+
+    // Buffer resources: A panel rows m0.., B panel rows n0.. (NT) or columns n0.. (NN).
+    const int a_rows = min(BM, p.M - m0);
+    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)((const char *)p.A + (size_t)m0 * K * 2), 0, a_rows * K * 2, 0x00020000);
+    __amdgpu_buffer_rsrc_t rsB;
+    if constexpr (!NN) {
+        const int b_rows = min(BN, N - n0);
+        rsB = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)p.B + (size_t)n0 * K * 2), 0,
+                                                b_rows * K * 2, 0x00020000);
+    } else {
+        rsB = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)p.B + (size_t)n0 * 2), 0,
+                                                (K * N - n0) * 2, 0x00020000);
+    }
+
+    // Per-lane source offsets of this wave's copies (relative to K tile 0) and
+    // the K position of each chunk (for the K tail).
+    uint32_t a_off[Cfg::A_LOADS];
+    int a_kc[Cfg::A_LOADS];
+#pragma unroll
+    for (int t = 0; t < Cfg::A_LOADS; ++t) {
+        int r, c;
+        k_tile_unit<BK>((t * WAVES + wave) * 64 + lane, r, c);
+        a_off[t] = (uint32_t)(r * K * 2 + c * 16);
+        a_kc[t] = c * 8;
+    }
+    uint32_t b_off[Cfg::B_LOADS];
+    int b_kc[Cfg::B_LOADS];
+#pragma unroll
+    for (int t = 0; t < Cfg::B_LOADS; ++t) {
+        const int u = (t * WAVES + wave) * 64 + lane;
+        if constexpr (!NN) {
+            int r, c;
+            k_tile_unit<BK>(u, r, c);
+            b_off[t] = (uint32_t)(r * K * 2 + c * 16);
+            b_kc[t] = c * 8;
+        } else {
+            int k, c;
+            n_tile_unit<BN>(u, k, c);
+            b_off[t] = (n0 + c * 8 < N) ? (uint32_t)(k * N * 2 + c * 16) : kOOB;
+            b_kc[t] = k;
+        }
+    }
+
+    // Issue all of this wave's copies of K tile kt into LDS slot `slot`.
+    const bool k_ragged = (K % BK) != 0;
+    auto issue = [&](int kt, int slot) {
+        char *dst = smem + slot * Cfg::SLOT_BYTES;
+        const bool tail = k_ragged && kt == nk - 1;
+        const int kbase = kt * BK;
+#pragma unroll
+        for (int t = 0; t < Cfg::A_LOADS; ++t) {
+            uint32_t off = a_off[t] + (uint32_t)kbase * 2;
+            if (tail && kbase + a_kc[t] >= K)
+                off = kOOB;
+            copy_1k(rsA, dst + (t * WAVES + wave) * 1024, off);
+        }
+#pragma unroll
+        for (int t = 0; t < Cfg::B_LOADS; ++t) {
+            uint32_t off;
+            if constexpr (!NN) {
+                off = b_off[t] + (uint32_t)kbase * 2;
+                if (tail && kbase + b_kc[t] >= K)
+                    off = kOOB;
+            } else {
+                // rows k >= K lie at or past num_records: no explicit tail mask
+                off = b_off[t] == kOOB ? kOOB : b_off[t] + (uint32_t)kbase * N * 2;
+            }
+            copy_1k(rsB, dst + Cfg::A_BYTES + (t * WAVES + wave) * 1024, off);
+        }
+    };
+
+    // Per-lane LDS read offsets of the MFMA operands, per k-step.
+    const int lr = lane & 31, lh = lane >> 5;
+    int a_rd[Cfg::KSTEPS], b_rd[Cfg::KSTEPS];
+#pragma unroll
+    for (int kk = 0; kk < Cfg::KSTEPS; ++kk) {
+        // kswz is periodic in 32 rows, so the f-th / g-th 32-row block adds f * 32 * BK * 2
+        a_rd[kk] = k_tile_offset<BK>(wm * Cfg::TM + lr, 2 * kk + lh);
+        if constexpr (!NN)
+            b_rd[kk] = Cfg::A_BYTES + k_tile_offset<BK>(wn * Cfg::TN + lr, 2 * kk + lh);
+        else
+            b_rd[kk] = 0;
+    }
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int f = 0; f < FM; ++f)
+#pragma unroll
+        for (int g = 0; g < FN; ++g)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[f][g][v] = 0.0f;
+
+    auto compute = [&](const char *slot) {
+#pragma unroll
+        for (int kk = 0; kk < Cfg::KSTEPS; ++kk) {
+            frag a[FM], b[FN];
+#pragma unroll
+            for (int f = 0; f < FM; ++f)
+                a[f] = *(const frag *)(slot + a_rd[kk] + f * 32 * BK * 2);
+#pragma unroll
+            for (int g = 0; g < FN; ++g) {
+                if constexpr (!NN)
+                    b[g] = *(const frag *)(slot + b_rd[kk] + g * 32 * BK * 2);
+                else
+                    b[g] = load_b_nn<T, Cfg>(slot, kk, wn * Cfg::TN + g * 32, lane);
+            }
+#pragma unroll
+            for (int f = 0; f < FM; ++f)
+#pragma unroll
+                for (int g = 0; g < FN; ++g)
+                    acc[f][g] = E::mfma(b[g], a[f], acc[f][g]);
+        }
+    };
+
+    // The K loop for a ring of S slots; S is a compile-time constant inside,
+    // so every wait count is an immediate.
+    auto pipeline = [&](auto stages_c) {
+        constexpr int S = decltype(stages_c)::value;
+        if constexpr (S == 1) {
+            // one slot: the copy of round kt+1 may start only after every wave
+            // has finished computing round kt
+            for (int kt = 0; kt < nk; ++kt) {
+                issue(kt, 0);
+                wait_vmcnt<0>();
+                barrier();
+                compute(smem);
+                barrier();
+            }
+        } else {
+            // prologue: fill slots 0 .. S-2
+            const int pro = ring_prologue(S, nk);
+            for (int t = 0; t < pro; ++t)
+                issue(t, ring_slot(t, S));
+            int rs = 0, ws = S - 1, kt = 0;
+            // steady state: tile kt+S-1 is issued while tile kt is computed;
+            // tiles kt+1 .. kt+S-2 may still be in flight at the wait
+            for (; kt + S - 1 < nk; ++kt) {
+                wait_vmcnt<(S - 2) * Cfg::LOADS>();  // = ring_inflight(kt, S, nk) tiles
+                barrier();
+                issue(kt + S - 1, ws);
+                ws = ws + 1 == S ? 0 : ws + 1;
+                compute(smem + rs * Cfg::SLOT_BYTES);
+                rs = rs + 1 == S ? 0 : rs + 1;
+            }
+            // drain: nothing left to issue, fewer tiles in flight each round
+            for (; kt < nk; ++kt) {
+                wait_tiles<Cfg::LOADS>(ring_inflight(kt, S, nk));
+                barrier();
+                compute(smem + rs * Cfg::SLOT_BYTES);
+                rs = rs + 1 == S ? 0 : rs + 1;
+            }
+        }
+    };
+    switch (p.stages) {
+#define PG_STAGES_CASE(i)                                  \
+    case i:                                                \
+        if constexpr ((i - 2) * Cfg::LOADS <= 63)          \
+            pipeline(std::integral_constant<int, i>());    \
+        break;
+        PG_STAGES_CASE(1) PG_STAGES_CASE(2) PG_STAGES_CASE(3) PG_STAGES_CASE(4)
+        PG_STAGES_CASE(5) PG_STAGES_CASE(6) PG_STAGES_CASE(7) PG_STAGES_CASE(8)
+        PG_STAGES_CASE(9) PG_STAGES_CASE(10)
+#undef PG_STAGES_CASE
+    default:
+        break;  // rejected on the host
+    }
+
+    // Epilogue: lane holds C[m][n .. n+3] for m = row base + lr and
+    // n = column base + 8 q + 4 lh, q = 0..3, per 32x32 block.
+    T *C = (T *)p.C;
+    const int M = p.M;
+#pragma unroll
+    for (int f = 0; f < FM; ++f) {
+        const int m = m0 + wm * Cfg::TM + f * 32 + lr;
+        if (m >= M)
+            continue;
+        T *crow = C + (size_t)m * N;
+#pragma unroll
+        for (int g = 0; g < FN; ++g) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int n = n0 + wn * Cfg::TN + g * 32 + 8 * q + 4 * lh;
+                typename E::quad v;
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    v[r] = (T)acc[f][g][4 * q + r];
+                if (p.c_vec && n + 3 < N) {
+                    *(typename E::quad *)(crow + n) = v;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (n + r < N)
+                            crow[n + r] = v[r];
+                }
+            }
+        }
+    }
+}
+
+}  // namespace pipegemm

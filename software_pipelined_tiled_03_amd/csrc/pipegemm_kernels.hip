@@ -1,0 +1,38 @@
+// Kernel instantiations for one (element type, B layout) pair, selected by
+// PG_ELEM (_Float16 or __bf16) and PG_NN (0 = NT, 1 = NN) at compile time.
+#include "pipegemm_kernel.hpp"
+#include "pipegemm_launch.hpp"
+
+#include <mutex>
+
+#ifndef PG_ELEM
+#error "PG_ELEM must name the element type"
+#endif
+#ifndef PG_NN
+#error "PG_NN must be 0 or 1"
+#endif
+
+namespace pipegemm {
+
+template <class T, bool NN, int BM, int BN, int BK, int WM, int WN>
+hipError_t launch(const KernelArgs &args, int grid, int lds_bytes, hipStream_t stream)
+{
+    using Cfg = Tile<BM, BN, BK, WM, WN>;
+    static std::once_flag once;
+    static hipError_t attr_err = hipSuccess;
+    std::call_once(once, [] {
+        attr_err = hipFuncSetAttribute((const void *)&gemm_kernel<T, NN, Cfg>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    });
+    if (attr_err != hipSuccess)
+        return attr_err;
+    hipLaunchKernelGGL((gemm_kernel<T, NN, Cfg>), dim3(grid), dim3(Cfg::THREADS), lds_bytes, stream, args);
+    return hipGetLastError();
+}
+
+#define PG_INSTANTIATE(BM, BN, BK, WM, WN) \
+    template hipError_t launch<PG_ELEM, (PG_NN != 0), BM, BN, BK, WM, WN>(const KernelArgs &, int, int, hipStream_t);
+PG_TILE_LIST(PG_INSTANTIATE)
+#undef PG_INSTANTIATE
+
+}  // namespace pipegemm

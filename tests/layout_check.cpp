@@ -1,0 +1,170 @@
+// Host-side check of the LDS layouts and the ring schedule the GPU kernel uses
+// (software_pipelined_tiled_03_amd/csrc/pipegemm_layout.hpp), by enumeration:
+//  1. every 16-byte unit the direct-to-LDS copy writes lands where the MFMA
+//     operand reads look for it (K-contiguous and N-contiguous tiles);
+//  2. the transposed reads of the NN form deliver, lane by lane, exactly the
+//     k / n elements the 32x32x16 MFMA operand needs;
+//  3. the operand reads are free of LDS bank conflicts;
+//  4. over a ring of S slots, each tile's wait covers its own copy exactly, and
+//     no slot is overwritten while a tile in it is still to be read.
+// Prints one line per failure and exits non-zero on any.
+#include <cstdio>
+#include <set>
+
+#include "pipegemm_layout.hpp"
+
+using namespace pipegemm;
+
+static int failures = 0;
+#define CHECK(cond, ...)                       \
+    do {                                       \
+        if (!(cond)) {                         \
+            if (failures < 40) {               \
+                std::printf("FAIL: " __VA_ARGS__); \
+                std::printf("\n");             \
+            }                                  \
+            ++failures;                        \
+        }                                      \
+    } while (0)
+
+template <int BK>
+void check_k_tile(int rows)
+{
+    const int cpr = BK / 8;
+    for (int u = 0; u < rows * cpr; ++u) {
+        int r = 0, c = 0;
+        k_tile_unit<BK>(u, r, c);
+        CHECK(c >= 0 && c < cpr, "BK=%d unit %d: chunk %d out of row", BK, u, c);
+        CHECK(k_tile_offset<BK>(r, c) == u * 16, "BK=%d unit %d: written (%d,%d) read elsewhere", BK, u, r, c);
+    }
+    for (int r = 0; r < rows; ++r) {
+        CHECK(kswz<BK>(r) == kswz<BK>(r % 32), "BK=%d: swizzle of row %d differs from row %d", BK, r, r % 32);
+        for (int c = 0; c < cpr; ++c)
+            CHECK(k_tile_offset<BK>(r + 32, c) == k_tile_offset<BK>(r, c) + 32 * BK * 2,
+                  "BK=%d: 32-row blocks are not a fixed stride apart", BK);
+    }
+    // MFMA operand read: lane l reads row base + l%32, chunk 2kk + l/32
+    for (int base = 0; base < rows; base += 32)
+        for (int kk = 0; kk < BK / 16; ++kk) {
+            int unit[64];
+            for (int l = 0; l < 64; ++l)
+                unit[l] = k_tile_offset<BK>(base + l % 32, 2 * kk + l / 32) / 16;
+            for (int g = 0; g < 64; g += 8) {
+                std::set<int> s;
+                for (int l = g; l < g + 8; ++l)
+                    s.insert(unit[l] % 8);
+                CHECK(s.size() == 8, "BK=%d rows %d kk %d lanes %d..%d: bank conflict (8-lane groups)", BK, base,
+                      kk, g, g + 7);
+            }
+            for (int g = 0; g < 64; g += 16) {
+                std::set<int> s;
+                for (int l = g; l < g + 16; ++l)
+                    s.insert(unit[l] % 16);
+                CHECK(s.size() == 16, "BK=%d rows %d kk %d lanes %d..%d: bank conflict (16-lane groups)", BK,
+                      base, kk, g, g + 15);
+            }
+        }
+}
+
+template <int BN>
+void check_n_tile(int bk)
+{
+    const int cpr = BN / 8;
+    for (int u = 0; u < bk * cpr; ++u) {
+        int k = 0, c = 0;
+        n_tile_unit<BN>(u, k, c);
+        CHECK(c >= 0 && c < cpr, "BN=%d unit %d: chunk out of row", BN, u);
+        CHECK(n_tile_offset<BN>(k, c) == u * 16, "BN=%d unit %d: written (%d,%d) read elsewhere", BN, u, k, c);
+    }
+    // transposed reads: decode which (k, n) each loaded element is, apply the
+    // instruction's lane exchange, compare with what the MFMA operand needs
+    for (int kk = 0; kk < bk / 16; ++kk)
+        for (int ncol0 = 0; ncol0 < BN; ncol0 += 32)
+            for (int h = 0; h < 2; ++h) {
+                int lk[64][4], ln[64][4], word[64];
+                for (int l = 0; l < 64; ++l) {
+                    const int off = nn_tr_offset<BN>(l, kk, ncol0, h);
+                    CHECK(off % 8 == 0 && off >= 0 && off + 8 <= bk * BN * 2, "BN=%d: tr read offset %d", BN, off);
+                    word[l] = off / 4;
+                    const int k = off / (BN * 2);
+                    const int phys = (off % (BN * 2)) / 16;
+                    const int c = phys ^ nswz(k);
+                    for (int j = 0; j < 4; ++j) {
+                        lk[l][j] = k;
+                        ln[l][j] = c * 8 + (off % 16) / 2 + j;
+                    }
+                }
+                for (int l = 0; l < 64; ++l) {
+                    const int G = l / 16, i = l % 16;
+                    for (int e = 0; e < 4; ++e) {
+                        const int src = 16 * G + 4 * e + i / 4;
+                        const int k = lk[src][i % 4], n = ln[src][i % 4];
+                        CHECK(k == 16 * kk + 8 * (l / 32) + 4 * h + e && n == ncol0 + l % 32,
+                              "BN=%d kk=%d ncol0=%d h=%d lane %d elem %d: got (k=%d,n=%d)", BN, kk, ncol0, h, l, e,
+                              k, n);
+                    }
+                }
+                for (int g = 0; g < 64; g += 16) {
+                    std::set<int> banks;
+                    for (int l = g; l < g + 16; ++l) {
+                        banks.insert(word[l] % 32);
+                        banks.insert((word[l] + 1) % 32);
+                    }
+                    CHECK(banks.size() == 32, "BN=%d kk=%d h=%d lanes %d..%d: tr read bank conflict", BN, kk, h, g,
+                          g + 15);
+                }
+            }
+}
+
+void check_ring()
+{
+    for (int S = 2; S <= 10; ++S)
+        for (int nk = 1; nk <= 40; ++nk) {
+            int slot_tile[16];
+            for (int s = 0; s < 16; ++s)
+                slot_tile[s] = -1;
+            int issued = 0;
+            auto issue = [&](int t) {
+                const int s = ring_slot(t, S);
+                // the slot's previous tile must already have been read (tile < t - S + 1 + ... )
+                CHECK(slot_tile[s] < 0 || slot_tile[s] <= t - S, "S=%d nk=%d: tile %d overwrites unread tile %d", S,
+                      nk, t, slot_tile[s]);
+                slot_tile[s] = t;
+                CHECK(t == issued, "S=%d nk=%d: tiles issued out of order", S, nk);
+                ++issued;
+            };
+            const int pro = ring_prologue(S, nk);
+            for (int t = 0; t < pro; ++t)
+                issue(t);
+            for (int kt = 0; kt < nk; ++kt) {
+                // wait: the copies of tile kt are complete iff the number of tiles
+                // allowed in flight equals the number issued after kt
+                CHECK(ring_inflight(kt, S, nk) == issued - 1 - kt, "S=%d nk=%d kt=%d: wait %d, issued after kt %d",
+                      S, nk, kt, ring_inflight(kt, S, nk), issued - 1 - kt);
+                CHECK(ring_inflight(kt, S, nk) >= 0 && ring_inflight(kt, S, nk) <= S - 2, "in-flight bound");
+                // barrier: every wave has finished reading tile kt-1, so its slot may be reused
+                if (kt + S - 1 < nk)
+                    issue(kt + S - 1);
+                CHECK(slot_tile[ring_slot(kt, S)] == kt, "S=%d nk=%d: slot of tile %d holds tile %d", S, nk, kt,
+                      slot_tile[ring_slot(kt, S)]);
+            }
+            CHECK(issued == nk, "S=%d nk=%d: %d tiles issued", S, nk, issued);
+        }
+}
+
+int main()
+{
+    check_k_tile<32>(256);
+    check_k_tile<64>(256);
+    check_n_tile<128>(32);
+    check_n_tile<128>(64);
+    check_n_tile<256>(32);
+    check_n_tile<256>(64);
+    check_ring();
+    if (failures) {
+        std::printf("%d failures\n", failures);
+        return 1;
+    }
+    std::printf("layout and schedule invariants: OK\n");
+    return 0;
+}
