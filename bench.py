@@ -87,6 +87,13 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--no-context", action="store_true", help="skip the torch.matmul context timing")
+    ap.add_argument("--workload", default=HEADLINE["workload"], help="one of inputs.WORKLOADS")
+    ap.add_argument("--block", default=None, help="tile as BMxBNxBK (default: the headline tile)")
+    ap.add_argument("--stages", type=int, default=None)
+    ap.add_argument("--threads", type=int, default=None)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (HBM counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -104,7 +111,17 @@ def main():
         return 1
     pg.load()
 
-    w = inputs.workload(HEADLINE["workload"])
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "launches": 5}))
+        return 0
+
+    w = inputs.workload(args.workload)
     A, B, dA, dB = _device_inputs(w)
     fn = pg.gemm_nt if w.layout == "nt" else pg.gemm_nn
     C = torch.empty((w.M, w.N), dtype=dA.dtype, device="cuda")
@@ -113,7 +130,8 @@ def main():
     sweep = {}
     if not args.no_sweep:
         for label, wl, block, th, stages in SWEEPS:
-            assert wl == HEADLINE["workload"]
+            if wl != w.name:
+                continue
             row = {}
             for s in stages:
                 ms = time_gemm(fn, dA, dB, C, block, s, th, steps=30, warmup=5)
@@ -128,7 +146,9 @@ def main():
             sweep[label] = row
         sweep["rejected_256x256x64_S4"] = rej
 
-    block, stages, threads = HEADLINE["block"], HEADLINE["num_stages"], HEADLINE["threads"]
+    block = tuple(int(x) for x in args.block.split("x")) if args.block else HEADLINE["block"]
+    stages = args.stages if args.stages is not None else HEADLINE["num_stages"]
+    threads = args.threads if args.threads is not None else HEADLINE["threads"]
     ms = time_gemm(fn, dA, dB, C, block, stages, threads, steps=args.steps, warmup=args.warmup)
     tflops = flops / ms / 1e9
     _log("headline %s tile %s S=%d threads=%d: %.3f ms, %.1f TFLOP/s" % (w.name, block, stages, threads, ms, tflops))
@@ -136,6 +156,8 @@ def main():
     # context: the vendor library on the same operands
     ref = None
     try:
+        if args.no_context:
+            raise RuntimeError("skipped")
         torch.matmul(dA, dB.t())
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
@@ -165,10 +187,11 @@ def main():
         "higher_is_better": True,
         "scaling": "strong",
         "vs_baseline": None,
-        "dtype": "f16",
+        "dtype": "f16" if w.dtype == inputs.F16 else "bf16",
         "data": "synthetic",
-        "config": {"workload": "GEMM NT %dx%dx%d fp16 uniform[-1,1], fp32 accumulate" % (w.M, w.N, w.K),
-                   "M": w.M, "N": w.N, "K": w.K, "layout": "NT", "block": list(block),
+        "config": {"workload": "GEMM %s %dx%dx%d %s, fp32 accumulate" % (
+                       w.layout.upper(), w.M, w.N, w.K, "fp16 uniform[-1,1]" if w.dtype == inputs.F16 else "bf16 normal(0,1)"),
+                   "M": w.M, "N": w.N, "K": w.K, "layout": w.layout.upper(), "block": list(block),
                    "num_stages": stages, "threads": threads},
         "pct_peak": round(100 * tflops / PEAK_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",

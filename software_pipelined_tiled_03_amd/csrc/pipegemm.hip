@@ -126,9 +126,9 @@ int validate(int layout, int64_t M, int64_t N, int64_t K, int dtype, int bm, int
     const int s = stages < 1 ? 1 : stages;
     if (s > kMaxStages)
         return fail(GEMM_ERR_UNSUPPORTED, "num_stages above %d is not supported", kMaxStages);
-    if (s >= 2 && (int64_t)in->loads_per_wave * (s - 2) > 63)
+    if (s > ring_max_stages(in->loads_per_wave))
         return fail(GEMM_ERR_UNSUPPORTED,
-                    "%d stages x %d copies per wave exceed the 63 loads one wave can keep in flight", s,
+                    "%d stages with %d copies per wave per tile exceed the 63 loads one wave can keep in flight", s,
                     in->loads_per_wave);
     const int64_t lim = (int64_t)1 << 31;
     if (M >= lim || N >= lim || K >= lim)

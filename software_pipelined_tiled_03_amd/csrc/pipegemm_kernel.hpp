@@ -42,6 +42,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "pipegemm_layout.hpp"
 
@@ -197,6 +198,40 @@ __device__ __forceinline__ void map_tile(const KernelArgs &p, int &tm, int &tn)
     tn = in_group / gsize;
 }
 
+// Calls f(std::integral_constant<int, i>()) for i = 0 .. N-1, so the body can
+// use i in constant expressions (template arguments of scheduling hints).
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>)
+{
+    (f(std::integral_constant<int, I>()), ...);
+}
+
+template <int N, class F>
+__device__ __forceinline__ void static_for(F &&f)
+{
+    static_for_impl(f, std::make_integer_sequence<int, N>());
+}
+
+// Scheduling hint for one stretch of NM MFMAs: LDS reads (NR) go out as early
+// as possible, two per MFMA, and global loads (NL) are spread evenly after
+// them, so both issue while the matrix core is busy.
+template <int NM, int NR, int NL, int... I>
+__device__ __forceinline__ void interleave_impl(std::integer_sequence<int, I...>)
+{
+    ((__builtin_amdgcn_sched_group_barrier(0x008, 1, 0),
+      (2 * I < NR ? __builtin_amdgcn_sched_group_barrier(0x100, (NR - 2 * I) < 2 ? (NR - 2 * I) : 2, 0) : (void)0),
+      ((I + 1) * NL / NM - I * NL / NM > 0
+           ? __builtin_amdgcn_sched_group_barrier(0x020, (I + 1) * NL / NM - I * NL / NM, 0)
+           : (void)0)),
+     ...);
+}
+
+template <int NM, int NR, int NL>
+__device__ __forceinline__ void interleave()
+{
+    interleave_impl<NM, NR, NL>(std::make_integer_sequence<int, NM>());
+}
+
 // ---------------------------------------------------------------------------
 // NN form: MFMA operand from the N-contiguous B tile, two transposed reads
 // (see nn_tr_offset for the lane mapping).
@@ -252,7 +287,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
     }
 
     // Per-lane source offsets of this wave's copies (relative to K tile 0) and
-    // the K position of each chunk (for the K tail).
+    // the K position of each chunk within a tile (for the K bound).
     uint32_t a_off[Cfg::A_LOADS];
     int a_kc[Cfg::A_LOADS];
 #pragma unroll
@@ -280,30 +315,29 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
         }
     }
 
-    // Issue all of this wave's copies of K tile kt into LDS slot `slot`.
-    const bool k_ragged = (K % BK) != 0;
-    auto issue = [&](int kt, int slot) {
+    // Issue this wave's copies [first, last) of K tile kt into LDS slot
+    // `slot` (copy t < A_LOADS is a piece of the A tile, the rest of the B
+    // tile).  Chunks at or beyond K (the ragged last tile, or a tile past the
+    // end of K) get an out-of-range offset and land as zeros.
+    auto issue = [&](int kt, int slot, int first, int last) {
         char *dst = smem + slot * Cfg::SLOT_BYTES;
-        const bool tail = k_ragged && kt == nk - 1;
         const int kbase = kt * BK;
 #pragma unroll
         for (int t = 0; t < Cfg::A_LOADS; ++t) {
-            uint32_t off = a_off[t] + (uint32_t)kbase * 2;
-            if (tail && kbase + a_kc[t] >= K)
-                off = kOOB;
+            if (t < first || t >= last)
+                continue;
+            const uint32_t off = kbase + a_kc[t] < K ? a_off[t] + (uint32_t)kbase * 2 : kOOB;
             copy_1k(rsA, dst + (t * WAVES + wave) * 1024, off);
         }
 #pragma unroll
         for (int t = 0; t < Cfg::B_LOADS; ++t) {
+            if (Cfg::A_LOADS + t < first || Cfg::A_LOADS + t >= last)
+                continue;
             uint32_t off;
-            if constexpr (!NN) {
-                off = b_off[t] + (uint32_t)kbase * 2;
-                if (tail && kbase + b_kc[t] >= K)
-                    off = kOOB;
-            } else {
-                // rows k >= K lie at or past num_records: no explicit tail mask
-                off = b_off[t] == kOOB ? kOOB : b_off[t] + (uint32_t)kbase * N * 2;
-            }
+            if constexpr (!NN)
+                off = kbase + b_kc[t] < K ? b_off[t] + (uint32_t)kbase * 2 : kOOB;
+            else
+                off = kbase + b_kc[t] < K && b_off[t] != kOOB ? b_off[t] + (uint32_t)kbase * N * 2 : kOOB;
             copy_1k(rsB, dst + Cfg::A_BYTES + (t * WAVES + wave) * 1024, off);
         }
     };
@@ -330,26 +364,49 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
             for (int v = 0; v < 16; ++v)
                 acc[f][g][v] = 0.0f;
 
-    auto compute = [&](const char *slot) {
+    // MFMA operands, double-buffered: k-step kk computes from buffer kk & 1
+    // while the reads of k-step kk+1 fill the other one.
+    frag fa[2][FM], fb[2][FN];
+    auto read_operands = [&](const char *slot, int kk, int buf) {
 #pragma unroll
-        for (int kk = 0; kk < Cfg::KSTEPS; ++kk) {
-            frag a[FM], b[FN];
+        for (int f = 0; f < FM; ++f)
+            fa[buf][f] = *(const frag *)(slot + a_rd[kk] + f * 32 * BK * 2);
 #pragma unroll
-            for (int f = 0; f < FM; ++f)
-                a[f] = *(const frag *)(slot + a_rd[kk] + f * 32 * BK * 2);
-#pragma unroll
-            for (int g = 0; g < FN; ++g) {
-                if constexpr (!NN)
-                    b[g] = *(const frag *)(slot + b_rd[kk] + g * 32 * BK * 2);
-                else
-                    b[g] = load_b_nn<T, Cfg>(slot, kk, wn * Cfg::TN + g * 32, lane);
-            }
-#pragma unroll
-            for (int f = 0; f < FM; ++f)
-#pragma unroll
-                for (int g = 0; g < FN; ++g)
-                    acc[f][g] = E::mfma(b[g], a[f], acc[f][g]);
+        for (int g = 0; g < FN; ++g) {
+            if constexpr (!NN)
+                fb[buf][g] = *(const frag *)(slot + b_rd[kk] + g * 32 * BK * 2);
+            else
+                fb[buf][g] = load_b_nn<T, Cfg>(slot, kk, wn * Cfg::TN + g * 32, lane);
         }
+    };
+    // MFMAs [first, last) of one k-step, in row-major block order.
+    auto mfmas = [&](int buf, int first, int last) {
+#pragma unroll
+        for (int i = 0; i < FM * FN; ++i)
+            if (i >= first && i < last)
+                acc[i / FN][i % FN] = E::mfma(fb[buf][i % FN], fa[buf][i / FN], acc[i / FN][i % FN]);
+    };
+    constexpr int kMfma = FM * FN;
+    constexpr int kReads = FM + FN * (NN ? 2 : 1);
+    constexpr int kLast = Cfg::KSTEPS - 1;
+
+    // Copies of one tile spread over the k-steps of an iteration: k-step kk
+    // issues copies [kk * LOADS / KSTEPS, (kk + 1) * LOADS / KSTEPS).
+    constexpr int kL = Cfg::LOADS, kS = Cfg::KSTEPS;
+
+    // All k-steps of the tile in `slot` but the last; with `spread`, also the
+    // copies of tile `ctile` into slot `cslot` that belong to those k-steps.
+    auto tile_body = [&](const char *slot, auto spread_c, int ctile, int cslot) {
+        constexpr bool spread = decltype(spread_c)::value;
+        static_for<kLast>([&](auto kk_c) {
+            constexpr int kk = decltype(kk_c)::value;
+            read_operands(slot, kk + 1, (kk + 1) & 1);
+            if constexpr (spread)
+                issue(ctile, cslot, kk * kL / kS, (kk + 1) * kL / kS);
+            mfmas(kk & 1, 0, kMfma);
+            interleave<kMfma, kReads, spread ? (kk + 1) * kL / kS - kk * kL / kS : 0>();
+            __builtin_amdgcn_sched_barrier(0);
+        });
     };
 
     // The K loop for a ring of S slots; S is a compile-time constant inside,
@@ -358,44 +415,69 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
         constexpr int S = decltype(stages_c)::value;
         if constexpr (S == 1) {
             // one slot: the copy of round kt+1 may start only after every wave
-            // has finished computing round kt
+            // has finished computing round kt; copy and compute never overlap
             for (int kt = 0; kt < nk; ++kt) {
-                issue(kt, 0);
+                issue(kt, 0, 0, Cfg::LOADS);
                 wait_vmcnt<0>();
                 barrier();
-                compute(smem);
+#pragma unroll
+                for (int kk = 0; kk < Cfg::KSTEPS; ++kk) {
+                    read_operands(smem, kk, 0);
+                    mfmas(0, 0, kMfma);
+                }
                 barrier();
             }
         } else {
-            // prologue: fill slots 0 .. S-2
-            const int pro = ring_prologue(S, nk);
-            for (int t = 0; t < pro; ++t)
-                issue(t, ring_slot(t, S));
-            int rs = 0, ws = S - 1, kt = 0;
-            // steady state: tile kt+S-1 is issued while tile kt is computed;
-            // tiles kt+1 .. kt+S-2 may still be in flight at the wait
-            for (; kt + S - 1 < nk; ++kt) {
-                wait_vmcnt<(S - 2) * Cfg::LOADS>();  // = ring_inflight(kt, S, nk) tiles
+            constexpr bool spread = ring_spread(S);
+            // prologue (tiles past the end of K are all-zero copies, so every
+            // iteration below is identical and every wait is one immediate)
+#pragma unroll
+            for (int t = 0; t < ring_prologue(S); ++t)
+                issue(t, ring_slot(t, S), 0, kL);
+            wait_vmcnt<ring_wait_first(S) * kL>();
+            barrier();
+            read_operands(smem, 0, 0);
+            int rs = 0;                          // slot of tile kt
+            int cs = spread ? S - 1 : 0;         // slot the spread copies of iteration kt fill
+            for (int kt = 0; kt < nk; ++kt) {
+                const int nrs = rs + 1 == S ? 0 : rs + 1;
+                const int ctile = ring_issue_tile(kt, S);
+                tile_body(smem + rs * Cfg::SLOT_BYTES, std::integral_constant<bool, spread>(), ctile, cs);
+                // last k-step: its operands are in registers; once they have
+                // arrived this wave no longer reads tile kt's slot
+                wait_lds();
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (spread) {
+                    issue(ctile, cs, kLast * kL / kS, kL);
+                    mfmas(kLast & 1, 0, kMfma / 2);
+                    interleave<kMfma / 2, 0, kL - kLast * kL / kS>();
+                } else {
+                    mfmas(kLast & 1, 0, kMfma / 2);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                // tile kt+1 has landed once only the S-2 tiles issued after it
+                // may be in flight; after the barrier every wave is done with
+                // tile kt's slot and sees tile kt+1
+                wait_vmcnt<ring_wait_steady(S) * kL>();
                 barrier();
-                issue(kt + S - 1, ws);
-                ws = ws + 1 == S ? 0 : ws + 1;
-                compute(smem + rs * Cfg::SLOT_BYTES);
-                rs = rs + 1 == S ? 0 : rs + 1;
+                read_operands(smem + nrs * Cfg::SLOT_BYTES, 0, 0);
+                if constexpr (!spread)
+                    issue(ctile, rs, 0, kL);
+                mfmas(kLast & 1, kMfma / 2, kMfma);
+                interleave<kMfma - kMfma / 2, kReads, spread ? 0 : kL>();
+                __builtin_amdgcn_sched_barrier(0);
+                rs = nrs;
+                cs = cs + 1 == S ? 0 : cs + 1;
             }
-            // drain: nothing left to issue, fewer tiles in flight each round
-            for (; kt < nk; ++kt) {
-                wait_tiles<Cfg::LOADS>(ring_inflight(kt, S, nk));
-                barrier();
-                compute(smem + rs * Cfg::SLOT_BYTES);
-                rs = rs + 1 == S ? 0 : rs + 1;
-            }
+            // no copy may still be writing LDS when the workgroup ends
+            wait_vmcnt<0>();
         }
     };
     switch (p.stages) {
-#define PG_STAGES_CASE(i)                                  \
-    case i:                                                \
-        if constexpr ((i - 2) * Cfg::LOADS <= 63)          \
-            pipeline(std::integral_constant<int, i>());    \
+#define PG_STAGES_CASE(i)                                                                    \
+    case i:                                                                                  \
+        if constexpr (i <= ring_max_stages(Cfg::LOADS) && i * Cfg::SLOT_BYTES <= 160 * 1024) \
+            pipeline(std::integral_constant<int, i>());                                      \
         break;
         PG_STAGES_CASE(1) PG_STAGES_CASE(2) PG_STAGES_CASE(3) PG_STAGES_CASE(4)
         PG_STAGES_CASE(5) PG_STAGES_CASE(6) PG_STAGES_CASE(7) PG_STAGES_CASE(8)

@@ -87,19 +87,41 @@ PG_HD constexpr int nn_tr_offset(int lane, int kk, int ncol0, int h)
 }
 
 // ---------------------------------------------------------------------------
-// Pipeline schedule over a ring of S slots (S >= 2), nk K tiles.
-//   prologue: tile t (t < min(S-1, nk)) into slot t
-//   iteration kt: wait until at most ring_inflight(...) tiles issued after kt
-//   are outstanding, barrier, issue tile kt+S-1 (if any) into its slot,
-//   compute slot kt mod S.
+// Pipeline schedule over a ring of S slots (S >= 2), nk K tiles.  Tiles with
+// index >= nk are "padding" copies whose every chunk is out of range: they
+// write zeros and read no memory, and they make every iteration identical.
+//
+// Iteration j computes tile j from slot j mod S, each k-step reading the next
+// k-step's operands into registers.  Once every LDS read of tile j has
+// returned (during its last k-step) the wave waits until tile j+1 has landed,
+// passes a barrier (every wave is done with slot j mod S and sees tile j+1),
+// reads tile j+1's first operands and finishes tile j's last k-step from
+// registers.  A slot is refilled only after that barrier (chapter 11, section
+// 5.2: write a slot only after its last reader is done).
+//
+// Two ways to place the copies (both keep S-2 tiles in flight at each wait):
+//  - burst (S = 2): right after the barrier of iteration j, all copies of tile
+//    j+S into slot j mod S; the prologue issues tiles 0 .. S-1.
+//  - spread (S >= 3): during iteration j, before its wait, the copies of tile
+//    j+S-1 into slot (j-1) mod S (freed at the previous barrier), spread over
+//    the k-steps so the address unit takes them while the matrix cores run;
+//    the prologue issues tiles 0 .. S-2.
+// Either way the copy of tile t is issued one slot-turn after the tile S
+// places earlier has been read, which is the pages' rule that copy i may start
+// once compute i-S has finished.
 PG_HD constexpr int ring_slot(int tile, int S) { return tile % S; }
+PG_HD constexpr bool ring_spread(int S) { return S >= 3; }
+// tiles the prologue issues
+PG_HD constexpr int ring_prologue(int S) { return ring_spread(S) ? S - 1 : S; }
+// tiles issued after tile 0 that may stay in flight at its wait
+PG_HD constexpr int ring_wait_first(int S) { return ring_prologue(S) - 1; }
+// tiles issued after tile j+1 that may stay in flight at iteration j's wait
+PG_HD constexpr int ring_wait_steady(int S) { return S - 2; }
+// tile whose copies iteration j issues, and the slot they go to
+PG_HD constexpr int ring_issue_tile(int j, int S) { return ring_spread(S) ? j + S - 1 : j + S; }
 
-PG_HD constexpr int ring_prologue(int S, int nk) { return S - 1 < nk ? S - 1 : nk; }
-
-// Tiles issued after tile kt that may still be in flight at iteration kt's wait.
-PG_HD constexpr int ring_inflight(int kt, int S, int nk)
-{
-    return (S - 2) < (nk - 1 - kt) ? (S - 2) : (nk - 1 - kt);
-}
+// Deepest ring whose waits fit the 6-bit vmcnt, for `loads` copies per tile
+// per wave: at most S-1 tiles are in flight behind the one waited for.
+PG_HD constexpr int ring_max_stages(int loads) { return 1 + 63 / loads; }
 
 }  // namespace pipegemm

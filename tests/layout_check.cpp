@@ -119,37 +119,57 @@ void check_n_tile(int bk)
 void check_ring()
 {
     for (int S = 2; S <= 10; ++S)
-        for (int nk = 1; nk <= 40; ++nk) {
+        for (int nk = 0; nk <= 40; ++nk) {
             int slot_tile[16];
-            for (int s = 0; s < 16; ++s)
+            bool slot_read[16];
+            for (int s = 0; s < 16; ++s) {
                 slot_tile[s] = -1;
-            int issued = 0;
+                slot_read[s] = true;
+            }
+            int issued = 0, real = 0;
             auto issue = [&](int t) {
                 const int s = ring_slot(t, S);
-                // the slot's previous tile must already have been read (tile < t - S + 1 + ... )
-                CHECK(slot_tile[s] < 0 || slot_tile[s] <= t - S, "S=%d nk=%d: tile %d overwrites unread tile %d", S,
-                      nk, t, slot_tile[s]);
+                // a slot holding a real tile is refilled only after it was read
+                CHECK(slot_tile[s] < 0 || slot_tile[s] >= nk || slot_read[s],
+                      "S=%d nk=%d: tile %d overwrites unread tile %d", S, nk, t, slot_tile[s]);
+                CHECK(t == issued, "S=%d nk=%d: tiles issued out of order (%d, expected %d)", S, nk, t, issued);
                 slot_tile[s] = t;
-                CHECK(t == issued, "S=%d nk=%d: tiles issued out of order", S, nk);
+                slot_read[s] = false;
                 ++issued;
+                real += t < nk;
             };
-            const int pro = ring_prologue(S, nk);
-            for (int t = 0; t < pro; ++t)
+            // the wait for tile j is exact: it lets precisely the tiles issued
+            // after j stay in flight (copies complete in issue order)
+            auto wait_for = [&](int j, int allowed) {
+                CHECK(allowed == issued - 1 - j, "S=%d nk=%d: wait for tile %d allows %d, issued after it %d", S, nk,
+                      j, allowed, issued - 1 - j);
+                CHECK(slot_tile[ring_slot(j, S)] == j, "S=%d nk=%d: slot of tile %d holds %d", S, nk, j,
+                      slot_tile[ring_slot(j, S)]);
+            };
+            for (int t = 0; t < ring_prologue(S); ++t)
                 issue(t);
-            for (int kt = 0; kt < nk; ++kt) {
-                // wait: the copies of tile kt are complete iff the number of tiles
-                // allowed in flight equals the number issued after kt
-                CHECK(ring_inflight(kt, S, nk) == issued - 1 - kt, "S=%d nk=%d kt=%d: wait %d, issued after kt %d",
-                      S, nk, kt, ring_inflight(kt, S, nk), issued - 1 - kt);
-                CHECK(ring_inflight(kt, S, nk) >= 0 && ring_inflight(kt, S, nk) <= S - 2, "in-flight bound");
-                // barrier: every wave has finished reading tile kt-1, so its slot may be reused
-                if (kt + S - 1 < nk)
-                    issue(kt + S - 1);
-                CHECK(slot_tile[ring_slot(kt, S)] == kt, "S=%d nk=%d: slot of tile %d holds tile %d", S, nk, kt,
-                      slot_tile[ring_slot(kt, S)]);
+            wait_for(0, ring_wait_first(S));
+            for (int j = 0; j < nk; ++j) {
+                CHECK(slot_tile[ring_slot(j, S)] == j, "S=%d nk=%d: tile %d not in its slot", S, nk, j);
+                if (ring_spread(S)) {
+                    // spread copies go out during iteration j, before its wait,
+                    // into the slot the previous barrier freed
+                    CHECK(ring_slot(ring_issue_tile(j, S), S) == ring_slot(j + S - 1, S), "spread slot");
+                    issue(ring_issue_tile(j, S));
+                }
+                slot_read[ring_slot(j, S)] = true;  // every LDS read of tile j has returned
+                wait_for(j + 1, ring_wait_steady(S));
+                // barrier
+                if (!ring_spread(S)) {
+                    CHECK(ring_slot(ring_issue_tile(j, S), S) == ring_slot(j, S), "burst refills the freed slot");
+                    issue(ring_issue_tile(j, S));
+                }
             }
-            CHECK(issued == nk, "S=%d nk=%d: %d tiles issued", S, nk, issued);
+            CHECK(real == nk, "S=%d nk=%d: %d real tiles issued", S, nk, real);
         }
+    for (int loads = 1; loads <= 32; ++loads)
+        CHECK((ring_max_stages(loads) - 1) * loads <= 63 && ring_max_stages(loads) * loads > 63,
+              "ring_max_stages(%d)", loads);
 }
 
 int main()

@@ -103,10 +103,11 @@ def test_unsupported_configurations():
     assert check(bm=64, bn=64, bk=32) == pg.GEMM_ERR_UNSUPPORTED
     assert check(th=1024) == pg.GEMM_ERR_UNSUPPORTED
     assert "no kernel built" in pg.last_error()
-    # 2 waves of 128x128x32 copy 8 KiB-pieces per wave per tile: 10 stages would
-    # need 64 loads in flight, one more than a wave can count
-    assert check(th=128, s=9) == pg.GEMM_OK
-    assert check(th=128, s=10) == pg.GEMM_ERR_UNSUPPORTED
+    # 2 waves of 128x128x32 each issue 8 1-KiB copies per tile; with S slots up
+    # to S-1 tiles are in flight behind the one waited for: 8 stages keep 56
+    # loads in flight, 9 stages would need 64, one more than a wave can count
+    assert check(th=128, s=8) == pg.GEMM_OK
+    assert check(th=128, s=9) == pg.GEMM_ERR_UNSUPPORTED
 
 
 def test_zero_stages_is_the_single_buffer():
