@@ -202,7 +202,7 @@ int run(int layout, const void *A, const void *B, void *C, int64_t M, int64_t N,
     a.tiles_m = (int)((M + bm - 1) / bm);
     a.tiles_n = (int)((N + bn - 1) / bn);
     a.group_m = a.tiles_m < 4 ? a.tiles_m : 4;
-    a.c_vec = (N % 4) == 0;
+    a.c_vec = (N % 8) == 0 && ((uintptr_t)C & 15) == 0;
     const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
     if (grid >= (1LL << 31))
         return fail(GEMM_ERR_UNSUPPORTED, "too many tiles");

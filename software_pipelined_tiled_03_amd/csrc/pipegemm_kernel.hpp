@@ -69,7 +69,7 @@ struct KernelArgs {
     int tiles_m;  // ceil(M / BM)
     int tiles_n;  // ceil(N / BN)
     int group_m;  // tile rows swept before advancing along N (L2 reuse)
-    int c_vec;    // 1 when C rows allow 8-byte stores (N % 4 == 0)
+    int c_vec;    // 1 when C rows allow 16-byte stores (N % 8 == 0, C 16-byte aligned)
 };
 
 // ---------------------------------------------------------------------------
@@ -487,32 +487,55 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
         break;  // rejected on the host
     }
 
-    // Epilogue: lane holds C[m][n .. n+3] for m = row base + lr and
-    // n = column base + 8 q + 4 lh, q = 0..3, per 32x32 block.
+    // Epilogue.  The ring is free once every copy has landed and every wave
+    // is past its last LDS read; each wave then stages its output through
+    // its own LDS strip (G blocks of 32 x 32 at a time) so that every global
+    // store writes 16 contiguous bytes per lane and whole row segments per
+    // instruction, instead of 8 bytes in each of 32 rows.
+    constexpr int G = cbuf_blocks(FN, Cfg::SLOT_BYTES / WAVES);
+    constexpr int CH = 4 * G;  // 16-byte chunks per strip row
+    static_assert(2048 * G * WAVES <= Cfg::SLOT_BYTES, "strips must fit in one ring slot");
+    wait_vmcnt<0>();
+    barrier();
+    char *strip = smem + wave * 2048 * G;
     T *C = (T *)p.C;
     const int M = p.M;
+    const int mw = m0 + wm * Cfg::TM, nw = n0 + wn * Cfg::TN;
 #pragma unroll
     for (int f = 0; f < FM; ++f) {
-        const int m = m0 + wm * Cfg::TM + f * 32 + lr;
-        if (m >= M)
-            continue;
-        T *crow = C + (size_t)m * N;
 #pragma unroll
-        for (int g = 0; g < FN; ++g) {
+        for (int gp = 0; gp < FN / G; ++gp) {
+            // MFMA layout -> strip: lane holds row lr, columns 32 gb + 8 q + 4 lh .. +3
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + wn * Cfg::TN + g * 32 + 8 * q + 4 * lh;
-                typename E::quad v;
+            for (int gb = 0; gb < G; ++gb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    v[r] = (T)acc[f][g][4 * q + r];
-                if (p.c_vec && n + 3 < N) {
-                    *(typename E::quad *)(crow + n) = v;
-                } else {
+                for (int q = 0; q < 4; ++q) {
+                    typename E::quad v;
 #pragma unroll
                     for (int r = 0; r < 4; ++r)
-                        if (n + r < N)
-                            crow[n + r] = v[r];
+                        v[r] = (T)acc[f][gp * G + gb][4 * q + r];
+                    *(typename E::quad *)(strip + cbuf_half_offset(lr, 4 * gb + q, lh, G)) = v;
+                }
+            // strip -> C: lane takes 16 bytes (8 columns) of one row
+#pragma unroll
+            for (int i = 0; i < 2 * G; ++i) {
+                const int idx = i * 64 + lane;
+                const int r = idx / CH, c = idx % CH;
+                i16x8 x = *(const i16x8 *)(strip + cbuf_chunk_offset(r, c, G));
+                if (hswz(r))
+                    x = __builtin_shufflevector(x, x, 4, 5, 6, 7, 0, 1, 2, 3);
+                const int m = mw + f * 32 + r;
+                const int n = nw + (gp * G) * 32 + c * 8;
+                if (m < M) {
+                    short *crow = (short *)(C + (size_t)m * N);
+                    if (p.c_vec && n + 7 < N) {
+                        *(i16x8 *)(crow + n) = x;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (n + e < N)
+                                crow[n + e] = x[e];
+                    }
                 }
             }
         }

@@ -87,6 +87,46 @@ PG_HD constexpr int nn_tr_offset(int lane, int kk, int ncol0, int h)
 }
 
 // ---------------------------------------------------------------------------
+// Epilogue staging buffer: each wave turns G of its 32 x 32 output blocks at a
+// time (one 32-row strip, 32 G columns, 2 bytes each) from the MFMA layout
+// into row-major order, so the global stores write whole row segments.
+//
+// Row r of the strip has 4 G 16-byte chunks.  The MFMA layout gives lane l
+// (l < 64) 4 consecutive columns of row l mod 32 (an 8-byte "half" of a
+// chunk); lanes 0..15 (and each further group of 16) write 16 different rows
+// at the same logical position, so both the chunk and the half are swizzled
+// by the row: chunk c goes to c ^ cswz(r) and half h to h ^ hswz(r).  Reading
+// back, lane i takes logical chunk i mod 4G of row i / 4G (16 bytes) and swaps
+// its halves when hswz(r) is 1.
+PG_HD constexpr int cswz(int r, int G)
+{
+    return G == 1 ? ((r >> 1) & 3) : (r & 7);
+}
+PG_HD constexpr int hswz(int r) { return (r >> 3) & 1; }
+
+// Byte offset of the 8-byte half h of logical chunk c in row r.
+PG_HD constexpr int cbuf_half_offset(int r, int c, int h, int G)
+{
+    return r * 64 * G + ((c ^ cswz(r, G)) << 4) + ((h ^ hswz(r)) << 3);
+}
+
+// Byte offset of the 16-byte physical chunk holding logical chunk c of row r.
+PG_HD constexpr int cbuf_chunk_offset(int r, int c, int G)
+{
+    return r * 64 * G + ((c ^ cswz(r, G)) << 4);
+}
+
+// Output blocks per strip: the largest power of two dividing FN whose strip
+// (2 KiB per block) fits in `region` bytes.
+PG_HD constexpr int cbuf_blocks(int FN, int region)
+{
+    int g = 1;
+    while (g * 2 <= FN && FN % (g * 2) == 0 && 2048 * g * 2 <= region)
+        g *= 2;
+    return g;
+}
+
+// ---------------------------------------------------------------------------
 // Pipeline schedule over a ring of S slots (S >= 2), nk K tiles.  Tiles with
 // index >= nk are "padding" copies whose every chunk is out of range: they
 // write zeros and read no memory, and they make every iteration identical.

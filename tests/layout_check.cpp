@@ -116,6 +116,45 @@ void check_n_tile(int bk)
             }
 }
 
+// Epilogue staging buffer for strips of G output blocks.
+void check_cbuf(int G)
+{
+    const int chunks = 4 * G, bytes = 32 * 64 * G;
+    std::set<int> written;
+    // every (row, column quad) lands in a distinct 8-byte slot inside the strip
+    for (int r = 0; r < 32; ++r)
+        for (int c = 0; c < chunks; ++c)
+            for (int h = 0; h < 2; ++h) {
+                const int off = cbuf_half_offset(r, c, h, G);
+                CHECK(off >= 0 && off + 8 <= bytes && off % 8 == 0, "G=%d: half offset %d", G, off);
+                CHECK(written.insert(off).second, "G=%d: (%d,%d,%d) overlaps", G, r, c, h);
+                // the read of logical chunk c of row r finds this half at 8 (h ^ hswz(r))
+                CHECK(cbuf_chunk_offset(r, c, G) + 8 * (h ^ hswz(r)) == off, "G=%d: read/write mismatch", G);
+            }
+    // writes: lane l of a 16-lane group writes row (l mod 32) at one logical
+    // (chunk, half); 16 lanes x 8 bytes must hit 16 distinct 8-byte bank pairs
+    for (int c = 0; c < chunks; ++c)
+        for (int h = 0; h < 2; ++h)
+            for (int g = 0; g < 64; g += 16) {
+                std::set<int> slots;
+                for (int l = g; l < g + 16; ++l)
+                    slots.insert((cbuf_half_offset(l % 32, c, (l / 32) ^ h, G) / 8) % 16);
+                CHECK(slots.size() == 16, "G=%d c=%d h=%d lanes %d..: epilogue write bank conflict", G, c, h, g);
+            }
+    // reads: lane i reads 16 bytes of row i / chunks; 8 lanes per LDS cycle
+    for (int base = 0; base < 32 * chunks; base += 64)
+        for (int g = 0; g < 64; g += 8) {
+            std::set<int> units;
+            for (int i = base + g; i < base + g + 8; ++i)
+                units.insert((cbuf_chunk_offset(i / chunks, i % chunks, G) / 16) % 8);
+            CHECK(units.size() == 8, "G=%d lanes %d..: epilogue read bank conflict", G, base + g);
+        }
+    // block choice
+    CHECK(cbuf_blocks(4, 8192) == 4 && cbuf_blocks(4, 6144) == 2 && cbuf_blocks(1, 2048) == 1 &&
+              cbuf_blocks(2, 16384) == 2,
+          "cbuf_blocks");
+}
+
 void check_ring()
 {
     for (int S = 2; S <= 10; ++S)
@@ -181,6 +220,9 @@ int main()
     check_n_tile<256>(32);
     check_n_tile<256>(64);
     check_ring();
+    check_cbuf(1);
+    check_cbuf(2);
+    check_cbuf(4);
     if (failures) {
         std::printf("%d failures\n", failures);
         return 1;
