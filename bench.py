@@ -20,13 +20,54 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA, published
-HEADLINE = dict(workload="nt_f16_4096", block=(256, 256, 64), num_stages=2, threads=256)
+HEADLINE = dict(workload="nt_f16_4096", block=(256, 256, 32), num_stages=3, threads=512)
 SWEEPS = [
     # (label, workload, block, threads, stages)
     ("tile128x128x32_t256", "nt_f16_4096", (128, 128, 32), 256, (1, 2, 3, 4, 6)),
-    ("tile256x256x32_t256", "nt_f16_4096", (256, 256, 32), 256, (1, 2, 3, 4)),
-    ("tile256x256x64_t256", "nt_f16_4096", (256, 256, 64), 256, (1, 2)),
+    ("tile256x256x32_t512", "nt_f16_4096", (256, 256, 32), 512, (1, 2, 3, 4, 5)),
+    ("tile256x256x32_t256", "nt_f16_4096", (256, 256, 32), 256, (1, 2, 3, 4, 5)),
+    ("tile256x256x64_t512", "nt_f16_4096", (256, 256, 64), 512, (1, 2)),
+    ("nn_bf16_tile128x128x32_t256", "nn_bf16_4096", (128, 128, 32), 256, (3,)),
+    ("nn_bf16_tile128x256x64_t256", "nn_bf16_4096", (128, 256, 64), 256, (3,)),
+    ("nn_bf16_tile256x128x32_t256", "nn_bf16_4096", (256, 128, 32), 256, (3,)),
 ]
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash():
+    """sha256 of the HIP sources and headers the kernels are built from."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "software_pipelined_tiled_03_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(block, stages, threads):
+    """HBM bytes per launch from a committed rocprofv3 summary of this exact
+    kernel configuration, or None if there is none or the kernel sources
+    changed since it was taken.  The summary carries lines
+    `config: <BMxBNxBK> S=<s> threads=<t>`, `source_sha256: <hex>` and
+    `hbm_bytes_per_launch: <int>`."""
+    want = "%dx%dx%d S=%d threads=%d" % (block[0], block[1], block[2], stages, threads)
+    src = kernel_source_hash()
+    if not os.path.isdir(PROFILES):
+        return None
+    for name in sorted(os.listdir(PROFILES)):
+        if not name.endswith(".md"):
+            continue
+        fields = {}
+        with open(os.path.join(PROFILES, name)) as f:
+            for line in f:
+                if ":" in line and not line.startswith("#"):
+                    k, v = line.split(":", 1)
+                    fields[k.strip("-* `")] = v.strip(" `\n")
+        if fields.get("config") == want and fields.get("source_sha256") == src and "hbm_bytes_per_launch" in fields:
+            return int(fields["hbm_bytes_per_launch"])
+    return None
 
 
 def _log(msg):
@@ -86,7 +127,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-context", action="store_true", help="skip the torch.matmul context timing")
     ap.add_argument("--workload", default=HEADLINE["workload"], help="one of inputs.WORKLOADS")
     ap.add_argument("--block", default=None, help="tile as BMxBNxBK (default: the headline tile)")
@@ -129,22 +170,32 @@ def main():
 
     sweep = {}
     if not args.no_sweep:
+        operands = {w.name: (dA, dB, C, fn)}
         for label, wl, block, th, stages in SWEEPS:
-            if wl != w.name:
-                continue
+            if wl not in operands:
+                ws = inputs.workload(wl)
+                _, _, sA, sB = _device_inputs(ws)
+                operands[wl] = (sA, sB, torch.empty((ws.M, ws.N), dtype=sA.dtype, device="cuda"),
+                                pg.gemm_nt if ws.layout == "nt" else pg.gemm_nn)
+            sA, sB, sC, sfn = operands[wl]
+            sflops = 2.0 * sA.shape[0] * sC.shape[1] * sA.shape[1]
             row = {}
             for s in stages:
-                ms = time_gemm(fn, dA, dB, C, block, s, th, steps=30, warmup=5)
-                row[str(s)] = dict(tflops=round(flops / ms / 1e9, 1), pct_peak=round(100 * flops / ms / 1e9 / PEAK_TFLOPS, 1),
+                ms = time_gemm(sfn, sA, sB, sC, block, s, th, steps=30, warmup=5)
+                row[str(s)] = dict(tflops=round(sflops / ms / 1e9, 1),
+                                   pct_peak=round(100 * sflops / ms / 1e9 / PEAK_TFLOPS, 1),
                                    lds_bytes=pg.gemm_lds_bytes(block[0], block[1], block[2], s))
-                _log("sweep %s S=%d: %.1f TFLOP/s" % (label, s, flops / ms / 1e9))
-            rej = None
+                _log("sweep %s S=%d: %.1f TFLOP/s" % (label, s, sflops / ms / 1e9))
+            sweep[label] = row
+        rej = None
+        nA, nB, nC, nfn = operands.get("nn_bf16_4096", (None, None, None, None))
+        if nfn is not None:
             try:
-                fn(dA, dB, out=C, block=(256, 256, 64), num_stages=4, threads=256)
+                nfn(nA, nB, out=nC, block=(256, 256, 64), num_stages=4, threads=256)
             except pg.LdsBudgetError as e:
                 rej = str(e)
-            sweep[label] = row
-        sweep["rejected_256x256x64_S4"] = rej
+        sweep["nn_bf16_256x256x64_S4_rejected"] = rej
+        del operands
 
     block = tuple(int(x) for x in args.block.split("x")) if args.block else HEADLINE["block"]
     stages = args.stages if args.stages is not None else HEADLINE["num_stages"]
@@ -195,7 +246,7 @@ def main():
                    "num_stages": stages, "threads": threads},
         "pct_peak": round(100 * tflops / PEAK_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(tflops / PEAK_TFLOPS, 4), "traffic": measured_traffic(block, stages, threads)},
         "cpu_baseline": cpu,
         "per_num_stages": sweep,
         "context_torch_matmul_tflops": ref,
