@@ -120,6 +120,7 @@ struct Tile {
     static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0,
                   "each wave must copy a whole number of 1 KiB pieces of each tile");
     static_assert(LOADS >= 1, "at least one copy per wave");
+    static_assert(BN >= 128, "the N-contiguous B tile swizzle needs 16 chunks per row");
 };
 
 // ---------------------------------------------------------------------------
@@ -235,20 +236,47 @@ __device__ __forceinline__ void interleave()
 // ---------------------------------------------------------------------------
 // NN form: MFMA operand from the N-contiguous B tile, two transposed reads
 // (see nn_tr_offset for the lane mapping).
+//
+// The reads are issued through inline assembly: for the ds_read_tr builtin the
+// compiler's wait insertion adds s_waitcnt vmcnt(0) before every read (it
+// cannot tell the read from the in-flight direct-to-LDS copies), which would
+// wait for every copy of the ring at every k-step.  The kernel orders copies
+// and reads itself (vmcnt waits and barriers); sync_nn_operands() supplies the
+// one thing the compiler no longer sees, the wait for the reads' data.
+__device__ __forceinline__ i16x4 ds_read_tr16_b64(const char *addr)
+{
+    i16x4 v;
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)addr;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(lds_addr) : "memory");
+    return v;
+}
+
 template <class T, class Cfg>
 __device__ __forceinline__ typename Elem<T>::frag load_b_nn(const char *slot, int kk, int ncol0, int lane)
 {
     i16x8 out;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const char *addr = slot + Cfg::A_BYTES + nn_tr_offset<Cfg::BN>(lane, kk, ncol0, h);
-        const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4 *)(addr));
+        const i16x4 v = ds_read_tr16_b64(slot + Cfg::A_BYTES + nn_tr_offset<Cfg::BN>(lane, kk, ncol0, h));
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             out[4 * h + e] = v[e];
     }
     return __builtin_bit_cast(typename Elem<T>::frag, out);
+}
+
+// Wait for every LDS read this wave issued (including the transposed reads
+// the compiler does not track) and make the B fragments depend on that wait,
+// so no MFMA reading them can be scheduled before it.
+template <class Frag, int FN>
+__device__ __forceinline__ void sync_nn_operands(Frag (&fb)[FN])
+{
+    // the builtin (not inline assembly), so the compiler's own wait
+    // bookkeeping also knows every earlier LDS read has completed
+    wait_lds();
+#pragma unroll
+    for (int g = 0; g < FN; ++g)
+        asm volatile("" : "+v"(fb[g]));
 }
 
 // ---------------------------------------------------------------------------
@@ -379,6 +407,13 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
                 fb[buf][g] = load_b_nn<T, Cfg>(slot, kk, wn * Cfg::TN + g * 32, lane);
         }
     };
+    // NN form: the operands in buffer `buf` have arrived before any MFMA uses
+    // them (called before the next k-step's reads are issued, so those stay
+    // in flight).
+    auto sync_operands = [&](int buf) {
+        if constexpr (NN)
+            sync_nn_operands(fb[buf]);
+    };
     // MFMAs [first, last) of one k-step, in row-major block order.
     auto mfmas = [&](int buf, int first, int last) {
 #pragma unroll
@@ -400,6 +435,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
         constexpr bool spread = decltype(spread_c)::value;
         static_for<kLast>([&](auto kk_c) {
             constexpr int kk = decltype(kk_c)::value;
+            sync_operands(kk & 1);
             read_operands(slot, kk + 1, (kk + 1) & 1);
             if constexpr (spread)
                 issue(ctile, cslot, kk * kL / kS, (kk + 1) * kL / kS);
@@ -423,6 +459,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
 #pragma unroll
                 for (int kk = 0; kk < Cfg::KSTEPS; ++kk) {
                     read_operands(smem, kk, 0);
+                    sync_operands(0);
                     mfmas(0, 0, kMfma);
                 }
                 barrier();
@@ -446,6 +483,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
                 // last k-step: its operands are in registers; once they have
                 // arrived this wave no longer reads tile kt's slot
                 wait_lds();
+                sync_operands(kLast & 1);
                 __builtin_amdgcn_sched_barrier(0);
                 if constexpr (spread) {
                     issue(ctile, cs, kLast * kL / kS, kL);

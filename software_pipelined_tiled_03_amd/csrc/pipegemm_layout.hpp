@@ -17,17 +17,19 @@ namespace pipegemm {
 // chunk c ^ kswz(r).
 //
 // MFMA operand reads have 32 consecutive lanes read one logical chunk of 32
-// consecutive rows (rows 32q .. 32q+31).  The swizzle maps any 8 consecutive
-// rows of such a block to 8 distinct 16-byte bank groups, and any 16
-// consecutive rows to 16 distinct positions modulo 16 chunks, so ds_read_b128
-// is conflict-free whether the LDS serves 8 or 16 lanes' 16 bytes per cycle.
-// It depends only on r mod 32, so a lane's swizzle is the same in every
-// 32-row block and block offsets become immediates.
+// consecutive rows (rows 32q .. 32q+31; lanes 32..63 read the next chunk).
+// Without a swizzle, rows 128 or 64 bytes apart fall on the same LDS banks.
+// The swizzles were chosen by measurement on gfx950 (rocprofv3
+// SQ_LDS_BANK_CONFLICT over every operand read the kernel issues): both read
+// patterns below run at the conflict-free rate of a contiguous ds_read_b128,
+// while e.g. ((r >> 1) ^ (r >> 3)) & 3 for BK = 32, or r & 7 for BK = 64,
+// cost twice that.  Both depend only on r mod 32, so a lane's swizzle is the
+// same in every 32-row block and block offsets become immediates.
 template <int BK>
 PG_HD constexpr int kswz(int r)
 {
     static_assert(BK == 32 || BK == 64, "block_K must be 32 or 64");
-    return BK == 64 ? ((r & 7) ^ ((r >> 3) & 1)) : (((r >> 1) ^ (r >> 3)) & 3);
+    return BK == 64 ? ((r & 7) ^ ((r >> 3) & 1)) : ((r >> 2) & 3);
 }
 
 // Byte offset, within a K-contiguous tile, of logical chunk c of row r.
@@ -50,11 +52,16 @@ PG_HD constexpr void k_tile_unit(int u, int &r, int &c)
 // ---------------------------------------------------------------------------
 // N-contiguous B tile (NN form): row k holds BN elements, BN/8 chunks; logical
 // chunk c of row k is stored at physical chunk c ^ nswz(k).  A transposed read
-// by 16 lanes touches 4 consecutive rows x 2 adjacent chunks (32 bytes each);
-// nswz puts the 4 rows' chunk pairs on 8 distinct 16-byte bank groups.
+// by 32 lanes (two 16-lane groups) touches 4 consecutive rows x 64 bytes; rows
+// are 256 or 512 bytes apart, so unswizzled they share banks.  nswz moves the
+// 4 rows' 64-byte pieces to the four different 64-byte quarters of a 256-byte
+// bank row, which
+// measures conflict-free on gfx950 (the rate of a contiguous
+// ds_read_b64_tr_b16); permuting chunks within 128 bytes only, e.g.
+// (k & 3) << 1, measures 1.8x slower.  Needs BN >= 128 (16 chunks per row).
 PG_HD constexpr int nswz(int k)
 {
-    return ((k & 3) << 1) ^ ((k >> 2) & 1);
+    return (k & 3) << 2;
 }
 
 template <int BN>
