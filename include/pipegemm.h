@@ -34,6 +34,14 @@
  *  - Validation order: (1) arguments, (2) LDS budget, (3) alignment,
  *    (4) supported configuration.  An over-budget request therefore always
  *    reports GEMM_ERR_LDS_BUDGET, whatever else is wrong with its tile.
+ *
+ * The a_lead option (an MI355X addition to the tutorial's ring): with a_lead = 1 the
+ * A tiles get a ring of num_stages + 1 LDS buffers and are copied one K step
+ * further ahead than the B tiles, which keep num_stages buffers.  It spends
+ * LDS a full extra stage would not fit in (256 x 256 x 64 tiles: two stages
+ * are 128 KiB, three would be 192 KiB; two stages plus one A tile are exactly
+ * gfx950's 160 KiB) on more copy latency hiding.  The result is bit-identical
+ * to a_lead = 0: only the order in which copies are issued changes.
  */
 #ifndef PIPEGEMM_H
 #define PIPEGEMM_H
@@ -57,7 +65,8 @@ enum gemm_layout {
 enum gemm_status {
     GEMM_OK = 0,
     GEMM_ERR_ARG = 1,         /* negative size, null pointer, unknown dtype/layout, bad block/stage/thread value */
-    GEMM_ERR_LDS_BUDGET = 2,  /* num_stages x (block_M + block_N) x block_K x 2 bytes exceeds the LDS limit */
+    GEMM_ERR_LDS_BUDGET = 2,  /* num_stages x (block_M + block_N) x block_K x 2 bytes (+ block_M x block_K x 2
+                                 with a_lead) exceeds the LDS limit */
     GEMM_ERR_UNSUPPORTED = 3, /* no kernel is built for this (dtype, layout, tile, threads) or size limits exceeded */
     GEMM_ERR_ALIGN = 4,       /* K (and N for NN) not a multiple of 8, or misaligned pointers */
     GEMM_ERR_HIP = 5          /* a HIP runtime call failed (no device, launch failure) */
@@ -82,13 +91,15 @@ enum gemm_status {
  *   num_stages  number of LDS ring buffers; 1 = single buffer, no overlap
  *               (the non-pipelined control); 0 = alias of 1 (a loop that is not
  *               pipelined is single-buffered)
+ *   a_lead      0, or 1 to give A one more buffer and copy it one K step
+ *               earlier (needs num_stages >= 2; built for num_stages <= 4)
  *   threads     threads per workgroup, a multiple of 64 (0 selects 256)
  *   hip_stream  hipStream_t to launch on, or NULL
  * Returns a gemm_status.  Partial tiles at the M, N and K edges are handled:
  * out-of-range A/B elements are read as zero and out-of-range C is never written.
  */
 int gemm_nt(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype,
-            int block_M, int block_N, int block_K, int num_stages, int threads, void *hip_stream);
+            int block_M, int block_N, int block_K, int num_stages, int a_lead, int threads, void *hip_stream);
 
 /*
  * gemm_nn: C[M,N] = A[M,K] . B[K,N].
@@ -99,18 +110,19 @@ int gemm_nt(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t
  * [K,N] row-major and N must also be a multiple of 8.
  */
 int gemm_nn(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype,
-            int block_M, int block_N, int block_K, int num_stages, int threads, void *hip_stream);
+            int block_M, int block_N, int block_K, int num_stages, int a_lead, int threads, void *hip_stream);
 
 /*
  * gemm_lds_bytes: LDS the pipeline of one workgroup needs,
- *   max(num_stages, 1) x (block_M x block_K + block_K x block_N) x 2 bytes.
+ *   max(num_stages, 1) x (block_M x block_K + block_K x block_N) x 2 bytes,
+ *   plus block_M x block_K x 2 bytes when a_lead is 1.
  *
  * Defined by: TileLang tutorial, chapter 11, section 4.5 (per-stage bytes of
  * the A and B tiles times the stage count; the accumulator lives in registers).
  * Pure host arithmetic.  Returns -1 for a negative block size, a negative stage
- * count or an unknown dtype.
+ * count, an a_lead other than 0 or 1, or an unknown dtype.
  */
-int64_t gemm_lds_bytes(int block_M, int block_N, int block_K, int num_stages, int dtype);
+int64_t gemm_lds_bytes(int block_M, int block_N, int block_K, int num_stages, int a_lead, int dtype);
 
 /*
  * gemm_lds_budget: the LDS limit of one workgroup on the current HIP device
@@ -128,7 +140,7 @@ int64_t gemm_lds_budget(void);
  * failure, never a slowdown).  Returns a gemm_status.
  */
 int gemm_check(int layout, int64_t M, int64_t N, int64_t K, int dtype, int block_M, int block_N,
-               int block_K, int num_stages, int threads, int64_t lds_budget);
+               int block_K, int num_stages, int a_lead, int threads, int64_t lds_budget);
 
 /*
  * gemm_last_error: message describing the last non-OK status returned on

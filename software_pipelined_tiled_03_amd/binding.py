@@ -74,13 +74,13 @@ def load():
     i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
     for name in ("gemm_nt", "gemm_nn"):
         f = getattr(lib, name)
-        f.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, vp]
+        f.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, i32, vp]
         f.restype = i32
-    lib.gemm_lds_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.gemm_lds_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.gemm_lds_bytes.restype = i64
     lib.gemm_lds_budget.argtypes = []
     lib.gemm_lds_budget.restype = i64
-    lib.gemm_check.argtypes = [i32, i64, i64, i64, i32, i32, i32, i32, i32, i32, i64]
+    lib.gemm_check.argtypes = [i32, i64, i64, i64, i32, i32, i32, i32, i32, i32, i32, i64]
     lib.gemm_check.restype = i32
     lib.gemm_last_error.argtypes = []
     lib.gemm_last_error.restype = ctypes.c_char_p
@@ -99,18 +99,20 @@ def _raise_for(status):
 
 # --- raw C-ABI mirrors (same names and arguments as the header) -------------
 
-def gemm_nt_raw(A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, threads, hip_stream):
+def gemm_nt_raw(A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, a_lead, threads, hip_stream):
     """gemm_nt on raw device addresses; returns the status code."""
-    return load().gemm_nt(A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, threads, hip_stream)
+    return load().gemm_nt(A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, a_lead, threads,
+                          hip_stream)
 
 
-def gemm_nn_raw(A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, threads, hip_stream):
+def gemm_nn_raw(A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, a_lead, threads, hip_stream):
     """gemm_nn on raw device addresses; returns the status code."""
-    return load().gemm_nn(A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, threads, hip_stream)
+    return load().gemm_nn(A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, a_lead, threads,
+                          hip_stream)
 
 
-def gemm_lds_bytes(block_M, block_N, block_K, num_stages, dtype=GEMM_F16) -> int:
-    return int(load().gemm_lds_bytes(block_M, block_N, block_K, num_stages, dtype))
+def gemm_lds_bytes(block_M, block_N, block_K, num_stages, dtype=GEMM_F16, a_lead=0) -> int:
+    return int(load().gemm_lds_bytes(block_M, block_N, block_K, num_stages, a_lead, dtype))
 
 
 def gemm_lds_budget() -> int:
@@ -120,9 +122,9 @@ def gemm_lds_budget() -> int:
     return v
 
 
-def gemm_check(layout, M, N, K, dtype, block_M, block_N, block_K, num_stages, threads, lds_budget) -> int:
+def gemm_check(layout, M, N, K, dtype, block_M, block_N, block_K, num_stages, threads, lds_budget, a_lead=0) -> int:
     """Validation only (status code); lds_budget > 0 touches no device."""
-    return int(load().gemm_check(layout, M, N, K, dtype, block_M, block_N, block_K, num_stages, threads,
+    return int(load().gemm_check(layout, M, N, K, dtype, block_M, block_N, block_K, num_stages, a_lead, threads,
                                  lds_budget))
 
 
@@ -137,7 +139,7 @@ def _dtype_code(t):
     raise GemmArgumentError(GEMM_ERR_ARG, "dtype must be float16 or bfloat16, got %s" % t.dtype)
 
 
-def _gemm(layout, A, B, out, block, num_stages, threads, stream):
+def _gemm(layout, A, B, out, block, num_stages, threads, stream, a_lead):
     import torch
     if A.dim() != 2 or B.dim() != 2:
         raise GemmArgumentError(GEMM_ERR_ARG, "A and B must be 2-D")
@@ -164,16 +166,16 @@ def _gemm(layout, A, B, out, block, num_stages, threads, stream):
     fn = load().gemm_nt if layout == GEMM_NT else load().gemm_nn
     with torch.cuda.device(A.device):
         st = fn(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K, _dtype_code(A), bm, bn, bk, num_stages,
-                threads, stream)
+                int(a_lead), threads, stream)
     _raise_for(st)
     return out
 
 
-def gemm_nt(A, B, out=None, block=(128, 128, 32), num_stages=3, threads=256, stream=None):
+def gemm_nt(A, B, out=None, block=(128, 128, 32), num_stages=3, threads=256, stream=None, a_lead=0):
     """C = A[M,K] @ B[N,K]^T on the GPU (fp16/bf16 in, fp32 accumulate, C in A's dtype)."""
-    return _gemm(GEMM_NT, A, B, out, block, num_stages, threads, stream)
+    return _gemm(GEMM_NT, A, B, out, block, num_stages, threads, stream, a_lead)
 
 
-def gemm_nn(A, B, out=None, block=(128, 128, 32), num_stages=3, threads=256, stream=None):
+def gemm_nn(A, B, out=None, block=(128, 128, 32), num_stages=3, threads=256, stream=None, a_lead=0):
     """C = A[M,K] @ B[K,N] on the GPU (fp16/bf16 in, fp32 accumulate, C in A's dtype)."""
-    return _gemm(GEMM_NN, A, B, out, block, num_stages, threads, stream)
+    return _gemm(GEMM_NN, A, B, out, block, num_stages, threads, stream, a_lead)

@@ -39,12 +39,13 @@ typedef hipError_t (*launch_fn)(const KernelArgs &, int grid, int lds_bytes, hip
 
 struct Instance {
     int dtype, layout, bm, bn, bk, threads;
-    int loads_per_wave;  // 1 KiB copies per wave per K tile (bounds the vmcnt wait)
+    int a_loads, b_loads;  // 1 KiB copies per wave per K tile of A and of B (bound the vmcnt wait)
     launch_fn launch;
 };
 
-#define PG_ROW(DT, T, LAYOUT, NN, BM, BN, BK, WM, WN) \
-    {DT, LAYOUT, BM, BN, BK, 64 * WM * WN, loads_per_wave(BM, BN, BK, WM * WN), &launch<T, NN, BM, BN, BK, WM, WN>},
+#define PG_ROW(DT, T, LAYOUT, NN, BM, BN, BK, WM, WN)                                                  \
+    {DT, LAYOUT, BM, BN, BK, 64 * WM * WN, loads_per_wave(BM, 0, BK, WM * WN), loads_per_wave(0, BN, BK, WM * WN), \
+     &launch<T, NN, BM, BN, BK, WM, WN>},
 #define PG_ROW_F16_NT(BM, BN, BK, WM, WN) PG_ROW(GEMM_F16, _Float16, GEMM_NT, false, BM, BN, BK, WM, WN)
 #define PG_ROW_BF16_NT(BM, BN, BK, WM, WN) PG_ROW(GEMM_BF16, __bf16, GEMM_NT, false, BM, BN, BK, WM, WN)
 #define PG_ROW_F16_NN(BM, BN, BK, WM, WN) PG_ROW(GEMM_F16, _Float16, GEMM_NN, true, BM, BN, BK, WM, WN)
@@ -66,10 +67,11 @@ const Instance *find_instance(int dtype, int layout, int bm, int bn, int bk, int
 
 constexpr int kDefaultThreads = 256;
 
-int64_t lds_bytes_of(int bm, int bn, int bk, int stages)
+// LDS of the two rings: S B tiles and S + lead A tiles (S = max(stages, 1)).
+int64_t lds_bytes_of(int bm, int bn, int bk, int stages, int lead)
 {
     const int64_t s = stages < 1 ? 1 : stages;
-    return s * ((int64_t)bm * bk + (int64_t)bk * bn) * 2;
+    return ((s + lead) * bm * (int64_t)bk + s * (int64_t)bk * bn) * 2;
 }
 
 // The checks shared by gemm_check and the launching entry points, in the
@@ -77,7 +79,7 @@ int64_t lds_bytes_of(int bm, int bn, int bk, int stages)
 // configuration.  On success *inst receives the kernel to launch.
 // ptrs is null for a size-only check; otherwise it holds A, B, C.
 int validate(int layout, int64_t M, int64_t N, int64_t K, int dtype, int bm, int bn, int bk, int stages,
-             int threads, int64_t budget, const void *const *ptrs, const Instance **inst)
+             int lead, int threads, int64_t budget, const void *const *ptrs, const Instance **inst)
 {
     // (1) arguments
     if (layout != GEMM_NT && layout != GEMM_NN)
@@ -91,6 +93,10 @@ int validate(int layout, int64_t M, int64_t N, int64_t K, int dtype, int bm, int
         return fail(GEMM_ERR_ARG, "block sizes must be positive (got %d x %d x %d)", bm, bn, bk);
     if (stages < 0)
         return fail(GEMM_ERR_ARG, "num_stages must be >= 0 (got %d)", stages);
+    if (lead != 0 && lead != 1)
+        return fail(GEMM_ERR_ARG, "a_lead must be 0 or 1 (got %d)", lead);
+    if (lead && stages < 2)
+        return fail(GEMM_ERR_ARG, "a_lead needs num_stages >= 2 (got %d)", stages);
     if (threads < 0 || threads % 64 != 0 || threads > 1024)
         return fail(GEMM_ERR_ARG, "threads must be 0 or a multiple of 64 up to 1024 (got %d)", threads);
     if (ptrs && M > 0 && N > 0) {
@@ -101,12 +107,19 @@ int validate(int layout, int64_t M, int64_t N, int64_t K, int dtype, int bm, int
     }
     if (budget <= 0)
         return fail(GEMM_ERR_ARG, "LDS budget must be positive");
-    // (2) LDS budget: num_stages x (A tile + B tile), checked before anything else about the tile
-    const int64_t need = lds_bytes_of(bm, bn, bk, stages);
-    if (need > budget)
+    // (2) LDS budget: num_stages x (A tile + B tile) (+ one A tile with lead),
+    // checked before anything else about the tile
+    const int64_t need = lds_bytes_of(bm, bn, bk, stages, lead);
+    if (need > budget) {
+        if (lead)
+            return fail(GEMM_ERR_LDS_BUDGET,
+                        "LDS budget exceeded: %d stage(s) x (%d x %d + %d x %d) x 2 B + one leading %d x %d A tile = "
+                        "%lld B > %lld B available",
+                        stages, bm, bk, bk, bn, bm, bk, (long long)need, (long long)budget);
         return fail(GEMM_ERR_LDS_BUDGET,
                     "LDS budget exceeded: %d stage(s) x (%d x %d + %d x %d) x 2 B = %lld B > %lld B available",
                     stages < 1 ? 1 : stages, bm, bk, bk, bn, (long long)need, (long long)budget);
+    }
     // (3) alignment: 16-byte copies along the contiguous dimension of A and B
     if (K % 8 != 0)
         return fail(GEMM_ERR_ALIGN, "K must be a multiple of 8 (got %lld)", (long long)K);
@@ -126,10 +139,14 @@ int validate(int layout, int64_t M, int64_t N, int64_t K, int dtype, int bm, int
     const int s = stages < 1 ? 1 : stages;
     if (s > kMaxStages)
         return fail(GEMM_ERR_UNSUPPORTED, "num_stages above %d is not supported", kMaxStages);
-    if (s > ring_max_stages(in->loads_per_wave))
+    if (lead && s > kMaxLeadStages)
+        return fail(GEMM_ERR_UNSUPPORTED, "a_lead is built for num_stages up to %d", kMaxLeadStages);
+    if (!ring_fits_vmcnt(s, lead, in->a_loads, in->b_loads))
         return fail(GEMM_ERR_UNSUPPORTED,
-                    "%d stages with %d copies per wave per tile exceed the 63 loads one wave can keep in flight", s,
-                    in->loads_per_wave);
+                    "%d stages%s with %d copies per wave per tile exceed the 63 loads one wave can keep in flight", s,
+                    lead ? " and a leading A tile" : "", in->a_loads + in->b_loads);
+    if (lds_bytes_of(bm, bn, bk, s, lead) > 160 * 1024)
+        return fail(GEMM_ERR_UNSUPPORTED, "no kernel is built for rings above 160 KiB of LDS");
     const int64_t lim = (int64_t)1 << 31;
     if (M >= lim || N >= lim || K >= lim)
         return fail(GEMM_ERR_UNSUPPORTED, "sizes must be below 2^31");
@@ -171,12 +188,12 @@ int device_budget(int64_t *out)
 }
 
 int run(int layout, const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype, int bm,
-        int bn, int bk, int stages, int threads, void *stream)
+        int bn, int bk, int stages, int lead, int threads, void *stream)
 {
     const void *ptrs[3] = {A, B, C};
     // Argument errors are reported as such even when no device can be queried:
     // run the checks once against an unlimited budget first.
-    int st = validate(layout, M, N, K, dtype, bm, bn, bk, stages, threads, 1LL << 40, ptrs, nullptr);
+    int st = validate(layout, M, N, K, dtype, bm, bn, bk, stages, lead, threads, 1LL << 40, ptrs, nullptr);
     if (st == GEMM_ERR_ARG)
         return st;
     int64_t budget = 0;
@@ -184,7 +201,7 @@ int run(int layout, const void *A, const void *B, void *C, int64_t M, int64_t N,
     if (st != GEMM_OK)
         return st;
     const Instance *in = nullptr;
-    st = validate(layout, M, N, K, dtype, bm, bn, bk, stages, threads, budget, ptrs, &in);
+    st = validate(layout, M, N, K, dtype, bm, bn, bk, stages, lead, threads, budget, ptrs, &in);
     if (st != GEMM_OK)
         return st;
     if (M == 0 || N == 0)
@@ -199,6 +216,7 @@ int run(int layout, const void *A, const void *B, void *C, int64_t M, int64_t N,
     a.K = (int)K;
     a.nk = (int)((K + bk - 1) / bk);
     a.stages = stages < 1 ? 1 : stages;
+    a.a_lead = lead;
     a.tiles_m = (int)((M + bm - 1) / bm);
     a.tiles_n = (int)((N + bn - 1) / bn);
     a.group_m = a.tiles_m < 4 ? a.tiles_m : 4;
@@ -206,7 +224,7 @@ int run(int layout, const void *A, const void *B, void *C, int64_t M, int64_t N,
     const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
     if (grid >= (1LL << 31))
         return fail(GEMM_ERR_UNSUPPORTED, "too many tiles");
-    const int lds = (int)lds_bytes_of(bm, bn, bk, a.stages);
+    const int lds = (int)lds_bytes_of(bm, bn, bk, a.stages, lead);
     hipError_t e = in->launch(a, (int)grid, lds, (hipStream_t)stream);
     if (e != hipSuccess)
         return fail(GEMM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -219,24 +237,25 @@ int run(int layout, const void *A, const void *B, void *C, int64_t M, int64_t N,
 extern "C" {
 
 int gemm_nt(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype, int block_M,
-            int block_N, int block_K, int num_stages, int threads, void *hip_stream)
+            int block_N, int block_K, int num_stages, int a_lead, int threads, void *hip_stream)
 {
-    return pipegemm::run(GEMM_NT, A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, threads,
+    return pipegemm::run(GEMM_NT, A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, a_lead, threads,
                          hip_stream);
 }
 
 int gemm_nn(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype, int block_M,
-            int block_N, int block_K, int num_stages, int threads, void *hip_stream)
+            int block_N, int block_K, int num_stages, int a_lead, int threads, void *hip_stream)
 {
-    return pipegemm::run(GEMM_NN, A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, threads,
+    return pipegemm::run(GEMM_NN, A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, a_lead, threads,
                          hip_stream);
 }
 
-int64_t gemm_lds_bytes(int block_M, int block_N, int block_K, int num_stages, int dtype)
+int64_t gemm_lds_bytes(int block_M, int block_N, int block_K, int num_stages, int a_lead, int dtype)
 {
-    if (block_M < 0 || block_N < 0 || block_K < 0 || num_stages < 0 || (dtype != GEMM_F16 && dtype != GEMM_BF16))
+    if (block_M < 0 || block_N < 0 || block_K < 0 || num_stages < 0 || (a_lead != 0 && a_lead != 1) ||
+        (dtype != GEMM_F16 && dtype != GEMM_BF16))
         return -1;
-    return pipegemm::lds_bytes_of(block_M, block_N, block_K, num_stages);
+    return pipegemm::lds_bytes_of(block_M, block_N, block_K, num_stages, a_lead);
 }
 
 int64_t gemm_lds_budget(void)
@@ -248,7 +267,7 @@ int64_t gemm_lds_budget(void)
 }
 
 int gemm_check(int layout, int64_t M, int64_t N, int64_t K, int dtype, int block_M, int block_N, int block_K,
-               int num_stages, int threads, int64_t lds_budget)
+               int num_stages, int a_lead, int threads, int64_t lds_budget)
 {
     int64_t budget = lds_budget;
     if (budget == 0) {
@@ -256,8 +275,8 @@ int gemm_check(int layout, int64_t M, int64_t N, int64_t K, int dtype, int block
         if (st != GEMM_OK)
             return st;
     }
-    return pipegemm::validate(layout, M, N, K, dtype, block_M, block_N, block_K, num_stages, threads, budget,
-                              nullptr, nullptr);
+    return pipegemm::validate(layout, M, N, K, dtype, block_M, block_N, block_K, num_stages, a_lead, threads,
+                              budget, nullptr, nullptr);
 }
 
 const char *gemm_last_error(void)

@@ -65,7 +65,8 @@ struct KernelArgs {
     void *C;
     int M, N, K;
     int nk;       // number of K tiles, ceil(K / BK)
-    int stages;   // LDS ring slots, >= 1
+    int stages;   // LDS ring slots of the B tile, >= 1
+    int a_lead;   // 1: the A tile runs one K tile further ahead in S + 1 slots (S >= 2)
     int tiles_m;  // ceil(M / BM)
     int tiles_n;  // ceil(N / BN)
     int group_m;  // tile rows swept before advancing along N (L2 reuse)
@@ -251,13 +252,14 @@ __device__ __forceinline__ i16x4 ds_read_tr16_b64(const char *addr)
     return v;
 }
 
+// `slot` is the B tile's slot.
 template <class T, class Cfg>
 __device__ __forceinline__ typename Elem<T>::frag load_b_nn(const char *slot, int kk, int ncol0, int lane)
 {
     i16x8 out;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const i16x4 v = ds_read_tr16_b64(slot + Cfg::A_BYTES + nn_tr_offset<Cfg::BN>(lane, kk, ncol0, h));
+        const i16x4 v = ds_read_tr16_b64(slot + nn_tr_offset<Cfg::BN>(lane, kk, ncol0, h));
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             out[4 * h + e] = v[e];
@@ -343,12 +345,10 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
         }
     }
 
-    // Issue this wave's copies [first, last) of K tile kt into LDS slot
-    // `slot` (copy t < A_LOADS is a piece of the A tile, the rest of the B
-    // tile).  Chunks at or beyond K (the ragged last tile, or a tile past the
-    // end of K) get an out-of-range offset and land as zeros.
-    auto issue = [&](int kt, int slot, int first, int last) {
-        char *dst = smem + slot * Cfg::SLOT_BYTES;
+    // Issue this wave's copies [first, last) of the A tile (B tile) of K tile
+    // kt into the slot at `dst`.  Chunks at or beyond K (the ragged last tile,
+    // or a tile past the end of K) get an out-of-range offset and land as zeros.
+    auto issue_a = [&](int kt, char *dst, int first, int last) {
         const int kbase = kt * BK;
 #pragma unroll
         for (int t = 0; t < Cfg::A_LOADS; ++t) {
@@ -357,16 +357,19 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
             const uint32_t off = kbase + a_kc[t] < K ? a_off[t] + (uint32_t)kbase * 2 : kOOB;
             copy_1k(rsA, dst + (t * WAVES + wave) * 1024, off);
         }
+    };
+    auto issue_b = [&](int kt, char *dst, int first, int last) {
+        const int kbase = kt * BK;
 #pragma unroll
         for (int t = 0; t < Cfg::B_LOADS; ++t) {
-            if (Cfg::A_LOADS + t < first || Cfg::A_LOADS + t >= last)
+            if (t < first || t >= last)
                 continue;
             uint32_t off;
             if constexpr (!NN)
                 off = kbase + b_kc[t] < K ? b_off[t] + (uint32_t)kbase * 2 : kOOB;
             else
                 off = kbase + b_kc[t] < K && b_off[t] != kOOB ? b_off[t] + (uint32_t)kbase * N * 2 : kOOB;
-            copy_1k(rsB, dst + Cfg::A_BYTES + (t * WAVES + wave) * 1024, off);
+            copy_1k(rsB, dst + (t * WAVES + wave) * 1024, off);
         }
     };
 
@@ -378,7 +381,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
         // kswz is periodic in 32 rows, so the f-th / g-th 32-row block adds f * 32 * BK * 2
         a_rd[kk] = k_tile_offset<BK>(wm * Cfg::TM + lr, 2 * kk + lh);
         if constexpr (!NN)
-            b_rd[kk] = Cfg::A_BYTES + k_tile_offset<BK>(wn * Cfg::TN + lr, 2 * kk + lh);
+            b_rd[kk] = k_tile_offset<BK>(wn * Cfg::TN + lr, 2 * kk + lh);
         else
             b_rd[kk] = 0;
     }
@@ -395,16 +398,16 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
     // MFMA operands, double-buffered: k-step kk computes from buffer kk & 1
     // while the reads of k-step kk+1 fill the other one.
     frag fa[2][FM], fb[2][FN];
-    auto read_operands = [&](const char *slot, int kk, int buf) {
+    auto read_operands = [&](const char *as, const char *bs, int kk, int buf) {
 #pragma unroll
         for (int f = 0; f < FM; ++f)
-            fa[buf][f] = *(const frag *)(slot + a_rd[kk] + f * 32 * BK * 2);
+            fa[buf][f] = *(const frag *)(as + a_rd[kk] + f * 32 * BK * 2);
 #pragma unroll
         for (int g = 0; g < FN; ++g) {
             if constexpr (!NN)
-                fb[buf][g] = *(const frag *)(slot + b_rd[kk] + g * 32 * BK * 2);
+                fb[buf][g] = *(const frag *)(bs + b_rd[kk] + g * 32 * BK * 2);
             else
-                fb[buf][g] = load_b_nn<T, Cfg>(slot, kk, wn * Cfg::TN + g * 32, lane);
+                fb[buf][g] = load_b_nn<T, Cfg>(bs, kk, wn * Cfg::TN + g * 32, lane);
         }
     };
     // NN form: the operands in buffer `buf` have arrived before any MFMA uses
@@ -425,102 +428,133 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
     constexpr int kReads = FM + FN * (NN ? 2 : 1);
     constexpr int kLast = Cfg::KSTEPS - 1;
 
-    // Copies of one tile spread over the k-steps of an iteration: k-step kk
-    // issues copies [kk * LOADS / KSTEPS, (kk + 1) * LOADS / KSTEPS).
-    constexpr int kL = Cfg::LOADS, kS = Cfg::KSTEPS;
+    constexpr int kLA = Cfg::A_LOADS, kLB = Cfg::B_LOADS, kS = Cfg::KSTEPS;
 
-    // All k-steps of the tile in `slot` but the last; with `spread`, also the
-    // copies of tile `ctile` into slot `cslot` that belong to those k-steps.
-    auto tile_body = [&](const char *slot, auto spread_c, int ctile, int cslot) {
-        constexpr bool spread = decltype(spread_c)::value;
-        static_for<kLast>([&](auto kk_c) {
-            constexpr int kk = decltype(kk_c)::value;
-            sync_operands(kk & 1);
-            read_operands(slot, kk + 1, (kk + 1) & 1);
-            if constexpr (spread)
-                issue(ctile, cslot, kk * kL / kS, (kk + 1) * kL / kS);
-            mfmas(kk & 1, 0, kMfma);
-            interleave<kMfma, kReads, spread ? (kk + 1) * kL / kS - kk * kL / kS : 0>();
-            __builtin_amdgcn_sched_barrier(0);
-        });
-    };
-
-    // The K loop for a ring of S slots; S is a compile-time constant inside,
-    // so every wait count is an immediate.
-    auto pipeline = [&](auto stages_c) {
+    // The K loop for a B ring of S slots and an A ring of S + LEAD slots
+    // (A slots first in LDS, then B slots); S and LEAD are compile-time
+    // constants inside, so every wait count is an immediate.
+    auto pipeline = [&](auto stages_c, auto lead_c) {
         constexpr int S = decltype(stages_c)::value;
+        constexpr int LEAD = decltype(lead_c)::value;
+        constexpr int SA = S + LEAD;
+        char *const ring_a = smem;
+        char *const ring_b = smem + SA * Cfg::A_BYTES;
         if constexpr (S == 1) {
             // one slot: the copy of round kt+1 may start only after every wave
             // has finished computing round kt; copy and compute never overlap
             for (int kt = 0; kt < nk; ++kt) {
-                issue(kt, 0, 0, Cfg::LOADS);
+                issue_a(kt, ring_a, 0, kLA);
+                issue_b(kt, ring_b, 0, kLB);
                 wait_vmcnt<0>();
                 barrier();
 #pragma unroll
                 for (int kk = 0; kk < Cfg::KSTEPS; ++kk) {
-                    read_operands(smem, kk, 0);
+                    read_operands(ring_a, ring_b, kk, 0);
                     sync_operands(0);
                     mfmas(0, 0, kMfma);
                 }
                 barrier();
             }
         } else {
-            constexpr bool spread = ring_spread(S);
+            constexpr bool spread = ring_spread(S, LEAD);
             // prologue (tiles past the end of K are all-zero copies, so every
             // iteration below is identical and every wait is one immediate)
 #pragma unroll
-            for (int t = 0; t < ring_prologue(S); ++t)
-                issue(t, ring_slot(t, S), 0, kL);
-            wait_vmcnt<ring_wait_first(S) * kL>();
+            for (int t = 0; t < ring_prologue(S, LEAD); ++t) {
+                issue_a(t, ring_a + ring_slot(t, SA) * Cfg::A_BYTES, 0, kLA);
+                issue_b(t, ring_b + ring_slot(t, S) * Cfg::B_BYTES, 0, kLB);
+            }
+            if constexpr (LEAD)
+                issue_a(S - 1, ring_a + ring_slot(S - 1, SA) * Cfg::A_BYTES, 0, kLA);
+            wait_vmcnt<ring_wait_first(S, LEAD, kLA, kLB)>();
             barrier();
-            read_operands(smem, 0, 0);
-            int rs = 0;                          // slot of tile kt
-            int cs = spread ? S - 1 : 0;         // slot the spread copies of iteration kt fill
+            read_operands(ring_a, ring_b, 0, 0);
+            int ra = 0, rb = 0;  // A and B slots of tile kt
             for (int kt = 0; kt < nk; ++kt) {
-                const int nrs = rs + 1 == S ? 0 : rs + 1;
-                const int ctile = ring_issue_tile(kt, S);
-                tile_body(smem + rs * Cfg::SLOT_BYTES, std::integral_constant<bool, spread>(), ctile, cs);
+                const int na = ra + 1 == SA ? 0 : ra + 1, nb = rb + 1 == S ? 0 : rb + 1;
+                const char *as = ring_a + ra * Cfg::A_BYTES, *bs = ring_b + rb * Cfg::B_BYTES;
+                // spread copies go to the slots freed at the previous barrier
+                char *cas = ring_a + (ra == 0 ? SA - 1 : ra - 1) * Cfg::A_BYTES;
+                char *cbs = ring_b + (rb == 0 ? S - 1 : rb - 1) * Cfg::B_BYTES;
+                const int ta = ring_issue_tile_a(kt, S, LEAD), tb = ring_issue_tile_b(kt, S, LEAD);
+                // the copies k-step kk issues (before its wait, in the last one)
+                auto copies = [&](auto kk_c, auto kk_end_c) {
+                    constexpr int k0 = decltype(kk_c)::value, k1 = decltype(kk_end_c)::value;
+                    constexpr int a0 = copy_a_before(k0, kS, kLA, kLB, LEAD), a1 = copy_a_before(k1, kS, kLA, kLB, LEAD);
+                    constexpr int b0 = copy_b_before(k0, kS, kLA, kLB, LEAD), b1 = copy_b_before(k1, kS, kLA, kLB, LEAD);
+                    if constexpr (spread) {
+                        if constexpr (LEAD) {
+                            issue_b(tb, cbs, b0, b1);
+                            issue_a(ta, cas, a0, a1);
+                        } else {
+                            issue_a(ta, cas, a0, a1);
+                            issue_b(tb, cbs, b0, b1);
+                        }
+                    }
+                    return std::integral_constant<int, spread ? (a1 - a0) + (b1 - b0) : 0>();
+                };
+                // every k-step but the last
+                static_for<kLast>([&](auto kk_c) {
+                    constexpr int kk = decltype(kk_c)::value;
+                    sync_operands(kk & 1);
+                    read_operands(as, bs, kk + 1, (kk + 1) & 1);
+                    auto nl = copies(kk_c, std::integral_constant<int, kk + 1>());
+                    mfmas(kk & 1, 0, kMfma);
+                    interleave<kMfma, kReads, decltype(nl)::value>();
+                    __builtin_amdgcn_sched_barrier(0);
+                });
                 // last k-step: its operands are in registers; once they have
-                // arrived this wave no longer reads tile kt's slot
+                // arrived this wave no longer reads tile kt's slots
                 wait_lds();
                 sync_operands(kLast & 1);
                 __builtin_amdgcn_sched_barrier(0);
-                if constexpr (spread) {
-                    issue(ctile, cs, kLast * kL / kS, kL);
-                    mfmas(kLast & 1, 0, kMfma / 2);
-                    interleave<kMfma / 2, 0, kL - kLast * kL / kS>();
-                } else {
-                    mfmas(kLast & 1, 0, kMfma / 2);
-                }
+                auto nl = copies(std::integral_constant<int, kLast>(), std::integral_constant<int, kS>());
+                mfmas(kLast & 1, 0, kMfma / 2);
+                interleave<kMfma / 2, 0, decltype(nl)::value>();
                 __builtin_amdgcn_sched_barrier(0);
-                // tile kt+1 has landed once only the S-2 tiles issued after it
-                // may be in flight; after the barrier every wave is done with
-                // tile kt's slot and sees tile kt+1
-                wait_vmcnt<ring_wait_steady(S) * kL>();
+                // tile kt+1 has landed once only the copies issued after its
+                // last B copy may be in flight; after the barrier every wave is
+                // done with tile kt's slots and sees tile kt+1
+                wait_vmcnt<ring_wait_steady(S, LEAD, kLA, kLB)>();
                 barrier();
-                read_operands(smem + nrs * Cfg::SLOT_BYTES, 0, 0);
-                if constexpr (!spread)
-                    issue(ctile, rs, 0, kL);
+                read_operands(ring_a + na * Cfg::A_BYTES, ring_b + nb * Cfg::B_BYTES, 0, 0);
+                if constexpr (!spread) {
+                    // burst: tile kt+S into the slots tile kt just freed
+                    issue_a(tb, (char *)as, 0, kLA);
+                    issue_b(tb, (char *)bs, 0, kLB);
+                }
                 mfmas(kLast & 1, kMfma / 2, kMfma);
-                interleave<kMfma - kMfma / 2, kReads, spread ? 0 : kL>();
+                interleave<kMfma - kMfma / 2, kReads, spread ? 0 : kLA + kLB>();
                 __builtin_amdgcn_sched_barrier(0);
-                rs = nrs;
-                cs = cs + 1 == S ? 0 : cs + 1;
+                ra = na;
+                rb = nb;
             }
             // no copy may still be writing LDS when the workgroup ends
             wait_vmcnt<0>();
         }
     };
+    // Instantiated rings: the B ring fits in 160 KiB with the A ring, and the
+    // copies in flight fit the 6-bit vmcnt.
+#define PG_RING_OK(i, l)                                                                                \
+    ((i) >= 1 && ((l) == 0 || ((i) >= 2 && (i) <= kMaxLeadStages)) &&                                   \
+     ring_fits_vmcnt((i), (l), Cfg::A_LOADS, Cfg::B_LOADS) &&                                            \
+     ring_lds_bytes((i), (l), Cfg::A_BYTES, Cfg::B_BYTES) <= 160 * 1024)
     switch (p.stages) {
-#define PG_STAGES_CASE(i)                                                                    \
-    case i:                                                                                  \
-        if constexpr (i <= ring_max_stages(Cfg::LOADS) && i * Cfg::SLOT_BYTES <= 160 * 1024) \
-            pipeline(std::integral_constant<int, i>());                                      \
+#define PG_STAGES_CASE(i)                                                          \
+    case i:                                                                        \
+        if (p.a_lead) {                                                            \
+            if constexpr (PG_RING_OK(i, 1))                                        \
+                pipeline(std::integral_constant<int, i>(), std::integral_constant<int, 1>()); \
+        } else {                                                                   \
+            if constexpr (PG_RING_OK(i, 0))                                        \
+                pipeline(std::integral_constant<int, i>(), std::integral_constant<int, 0>()); \
+        }                                                                          \
         break;
         PG_STAGES_CASE(1) PG_STAGES_CASE(2) PG_STAGES_CASE(3) PG_STAGES_CASE(4)
         PG_STAGES_CASE(5) PG_STAGES_CASE(6) PG_STAGES_CASE(7) PG_STAGES_CASE(8)
         PG_STAGES_CASE(9) PG_STAGES_CASE(10)
 #undef PG_STAGES_CASE
+#undef PG_RING_OK
     default:
         break;  // rejected on the host
     }

@@ -17,7 +17,8 @@ constexpr int kMaxStages = 10;
 template <class T, bool NN, int BM, int BN, int BK, int WM, int WN>
 hipError_t launch(const KernelArgs &args, int grid, int lds_bytes, hipStream_t stream);
 
-// 1 KiB copies each wave issues per K tile (bounds the copy wait, 63 loads).
+// 1 KiB copies each wave issues per K tile (bounds the copy wait, 63 loads);
+// loads_per_wave(bm, 0, bk, w) counts the A tile's alone, (0, bn, bk, w) B's.
 constexpr int loads_per_wave(int bm, int bn, int bk, int waves)
 {
     return (bm + bn) * bk * 2 / (1024 * waves);

@@ -134,41 +134,95 @@ PG_HD constexpr int cbuf_blocks(int FN, int region)
 }
 
 // ---------------------------------------------------------------------------
-// Pipeline schedule over a ring of S slots (S >= 2), nk K tiles.  Tiles with
-// index >= nk are "padding" copies whose every chunk is out of range: they
-// write zeros and read no memory, and they make every iteration identical.
+// Pipeline schedule.  The A tiles live in a ring of S + lead slots and the B
+// tiles in a ring of S slots (lead = 0 or 1); tile t uses A slot t mod (S +
+// lead) and B slot t mod S.  Tiles with index >= nk are "padding" copies whose
+// every chunk is out of range: they write zeros and read no memory, and they
+// make every iteration identical.
 //
-// Iteration j computes tile j from slot j mod S, each k-step reading the next
-// k-step's operands into registers.  Once every LDS read of tile j has
-// returned (during its last k-step) the wave waits until tile j+1 has landed,
-// passes a barrier (every wave is done with slot j mod S and sees tile j+1),
-// reads tile j+1's first operands and finishes tile j's last k-step from
-// registers.  A slot is refilled only after that barrier (chapter 11, section
-// 5.2: write a slot only after its last reader is done).
+// Iteration j computes tile j, each k-step reading the next k-step's operands
+// into registers.  Once every LDS read of tile j has returned (during its last
+// k-step) the wave waits until tile j+1 has landed, passes a barrier (every
+// wave is done with tile j's slots and sees tile j+1), reads tile j+1's first
+// operands and finishes tile j's last k-step from registers.  A slot is
+// refilled only after that barrier (chapter 11, section 5.2: write a slot only
+// after its last reader is done).
 //
-// Two ways to place the copies (both keep S-2 tiles in flight at each wait):
-//  - burst (S = 2): right after the barrier of iteration j, all copies of tile
-//    j+S into slot j mod S; the prologue issues tiles 0 .. S-1.
-//  - spread (S >= 3): during iteration j, before its wait, the copies of tile
-//    j+S-1 into slot (j-1) mod S (freed at the previous barrier), spread over
-//    the k-steps so the address unit takes them while the matrix cores run;
-//    the prologue issues tiles 0 .. S-2.
-// Either way the copy of tile t is issued one slot-turn after the tile S
-// places earlier has been read, which is the pages' rule that copy i may start
-// once compute i-S has finished.
-PG_HD constexpr int ring_slot(int tile, int S) { return tile % S; }
-PG_HD constexpr bool ring_spread(int S) { return S >= 3; }
-// tiles the prologue issues
-PG_HD constexpr int ring_prologue(int S) { return ring_spread(S) ? S - 1 : S; }
-// tiles issued after tile 0 that may stay in flight at its wait
-PG_HD constexpr int ring_wait_first(int S) { return ring_prologue(S) - 1; }
-// tiles issued after tile j+1 that may stay in flight at iteration j's wait
-PG_HD constexpr int ring_wait_steady(int S) { return S - 2; }
-// tile whose copies iteration j issues, and the slot they go to
-PG_HD constexpr int ring_issue_tile(int j, int S) { return ring_spread(S) ? j + S - 1 : j + S; }
+// Three ways to place the copies:
+//  - burst (S = 2, lead 0): right after the barrier of iteration j, all copies
+//    of tile j+S into the slots of tile j; the prologue issues tiles 0 .. S-1.
+//  - spread (S >= 3, lead 0): during iteration j, before its wait, the copies
+//    of tile j+S-1 into the slots of tile j-1 (freed at the previous barrier),
+//    spread evenly over the k-steps (A pieces first) so the address unit takes
+//    them while the matrix cores run; the prologue issues tiles 0 .. S-2.
+//  - lead (S >= 2, lead 1): the A tile runs one tile further ahead.  During
+//    iteration j the B copies of tile j+S-1 go out over the first half of the
+//    k-steps and the A copies of tile j+S over the second half, each into the
+//    slot its ring freed at the previous barrier; the prologue issues tiles
+//    0 .. S-2 and the A tile of tile S-1.  The B tile then has one iteration
+//    from its first copy to its wait, the A tile two.
+// In every mode the copies go out in the order A(t), B(t), A(t+1), B(t+1), ...
+// and the copy of a tile is issued one slot-turn after the tile its ring slot
+// held has been read, which is the pages' rule that copy i may start once
+// compute i-S has finished (with S + lead for the A ring).
+PG_HD constexpr int ring_slot(int tile, int slots) { return tile % slots; }
+PG_HD constexpr bool ring_spread(int S, int lead) { return lead ? S >= 2 : S >= 3; }
+// whole tiles the prologue issues (lead adds the A tile of the next one)
+PG_HD constexpr int ring_prologue(int S, int lead) { return ring_spread(S, lead) ? S - 1 : S; }
+// tile whose B copies iteration j issues, and tile whose A copies it issues
+PG_HD constexpr int ring_issue_tile_b(int j, int S, int lead)
+{
+    return ring_spread(S, lead) ? j + S - 1 : j + S;
+}
+PG_HD constexpr int ring_issue_tile_a(int j, int S, int lead)
+{
+    return ring_issue_tile_b(j, S, lead) + lead;
+}
+// copies (per wave) allowed in flight at the wait for tile 0, and at iteration
+// j's wait for tile j+1 (everything issued after that tile's last B copy)
+PG_HD constexpr int ring_wait_first(int S, int lead, int la, int lb)
+{
+    return ring_spread(S, lead) ? (S - 2) * (la + lb) + lead * la : (S - 1) * (la + lb);
+}
+PG_HD constexpr int ring_wait_steady(int S, int lead, int la, int lb)
+{
+    return (S - 2) * (la + lb) + lead * la;
+}
+// Copies one wave can have in flight at most (S-1 tiles and the leading A
+// tile); the 6-bit vmcnt bounds it at 63.
+PG_HD constexpr bool ring_fits_vmcnt(int S, int lead, int la, int lb)
+{
+    return (S - 1) * (la + lb) + lead * la <= 63;
+}
+// Deepest B ring built with lead (each lead ring is one more kernel variant).
+constexpr int kMaxLeadStages = 4;
 
-// Deepest ring whose waits fit the 6-bit vmcnt, for `loads` copies per tile
-// per wave: at most S-1 tiles are in flight behind the one waited for.
+// Deepest ring without lead whose waits fit the 6-bit vmcnt, for `loads`
+// copies per tile per wave.
 PG_HD constexpr int ring_max_stages(int loads) { return 1 + 63 / loads; }
+// LDS bytes of the two rings.
+PG_HD constexpr int ring_lds_bytes(int S, int lead, int a_bytes, int b_bytes)
+{
+    return (S + lead) * a_bytes + S * b_bytes;
+}
+
+// Spread placement of one iteration's copies over its ks k-steps: the A (B)
+// pieces issued before k-step kk, of la (lb) per wave.  Without lead the
+// sequence A pieces then B pieces is cut evenly over all k-steps; with lead the
+// B pieces are cut over the first half and the A pieces over the second half.
+PG_HD constexpr int spread_part(int kk, int k0, int k1, int n)
+{
+    return kk <= k0 ? 0 : (kk >= k1 ? n : (kk - k0) * n / (k1 - k0));
+}
+PG_HD constexpr int copy_a_before(int kk, int ks, int la, int lb, int lead)
+{
+    return lead ? spread_part(kk, ks / 2, ks, la)
+                : (spread_part(kk, 0, ks, la + lb) < la ? spread_part(kk, 0, ks, la + lb) : la);
+}
+PG_HD constexpr int copy_b_before(int kk, int ks, int la, int lb, int lead)
+{
+    return lead ? spread_part(kk, 0, ks / 2, lb)
+                : (spread_part(kk, 0, ks, la + lb) > la ? spread_part(kk, 0, ks, la + lb) - la : 0);
+}
 
 }  // namespace pipegemm

@@ -10,6 +10,8 @@
 // Prints one line per failure and exits non-zero on any.
 #include <cstdio>
 #include <set>
+#include <vector>
+#include <algorithm>
 
 #include "pipegemm_layout.hpp"
 
@@ -155,60 +157,119 @@ void check_cbuf(int G)
           "cbuf_blocks");
 }
 
+// Simulates the kernel's copy schedule piece by piece (every 1 KiB copy of a
+// wave, in issue order) for the three placements, and checks that a slot is
+// refilled only after its tile was read, that every wait leaves exactly the
+// copies issued after the awaited tile in flight, that each tile is read from
+// the slots its copies went to, and the 63-copy vmcnt bound.
+void check_ring_case(int S, int lead, int la, int lb, int ks, int nk)
+{
+    const int SA = S + lead;
+    struct Slot {
+        int tile = -1;
+        bool read = true;
+    };
+    std::vector<Slot> a_slots(SA), b_slots(S);
+    std::vector<int> last_a(nk + 2 * S + 4, -1), last_b(nk + 2 * S + 4, -1);  // index of a tile's last piece
+    int issued = 0, completed = 0, max_flight = 0;
+    int next_a = 0, next_b = 0;  // copies go out in tile order per operand
+    auto put = [&](std::vector<Slot> &ring, int t, bool is_a) {
+        Slot &sl = ring[ring_slot(t, is_a ? SA : S)];
+        if (sl.tile != t) {
+            CHECK(sl.tile < 0 || sl.tile >= nk || sl.read, "S=%d lead=%d nk=%d: %s tile %d overwrites unread tile %d",
+                  S, lead, nk, is_a ? "A" : "B", t, sl.tile);
+            sl.tile = t;
+            sl.read = false;
+        }
+        (is_a ? last_a : last_b)[t] = issued++;
+        max_flight = std::max(max_flight, issued - completed);
+    };
+    auto issue_a = [&](int t, int first, int last) {
+        for (int i = first; i < last; ++i) {
+            if (i == 0) {
+                CHECK(t == next_a, "S=%d lead=%d: A tile %d issued out of order", S, lead, t);
+                ++next_a;
+            }
+            put(a_slots, t, true);
+        }
+    };
+    auto issue_b = [&](int t, int first, int last) {
+        for (int i = first; i < last; ++i) {
+            if (i == 0) {
+                CHECK(t == next_b, "S=%d lead=%d: B tile %d issued out of order", S, lead, t);
+                ++next_b;
+            }
+            put(b_slots, t, false);
+        }
+    };
+    auto wait_for = [&](int j, int allowed) {
+        const int last = std::max(last_a[j], last_b[j]);
+        CHECK(last >= 0, "S=%d lead=%d nk=%d: tile %d never issued", S, lead, nk, j);
+        CHECK(allowed == issued - 1 - last, "S=%d lead=%d la=%d lb=%d nk=%d: wait for tile %d allows %d, %d after it",
+              S, lead, la, lb, nk, j, allowed, issued - 1 - last);
+        completed = std::max(completed, issued - allowed);
+        CHECK(a_slots[ring_slot(j, SA)].tile == j && b_slots[ring_slot(j, S)].tile == j,
+              "S=%d lead=%d nk=%d: tile %d not in its slots", S, lead, nk, j);
+    };
+    const bool spread = ring_spread(S, lead);
+    for (int t = 0; t < ring_prologue(S, lead); ++t) {
+        issue_a(t, 0, la);
+        issue_b(t, 0, lb);
+    }
+    if (lead)
+        issue_a(S - 1, 0, la);
+    wait_for(0, ring_wait_first(S, lead, la, lb));
+    for (int j = 0; j < nk; ++j) {
+        const int ta = ring_issue_tile_a(j, S, lead), tb = ring_issue_tile_b(j, S, lead);
+        for (int kk = 0; kk < ks; ++kk) {
+            if (spread) {
+                const int a0 = copy_a_before(kk, ks, la, lb, lead), a1 = copy_a_before(kk + 1, ks, la, lb, lead);
+                const int b0 = copy_b_before(kk, ks, la, lb, lead), b1 = copy_b_before(kk + 1, ks, la, lb, lead);
+                CHECK(a0 <= a1 && b0 <= b1, "plan not monotone");
+                if (lead) {
+                    issue_b(tb, b0, b1);
+                    issue_a(ta, a0, a1);
+                } else {
+                    issue_a(ta, a0, a1);
+                    issue_b(tb, b0, b1);
+                }
+            }
+            if (kk == ks - 1) {
+                // every LDS read of tile j has returned
+                a_slots[ring_slot(j, SA)].read = true;
+                b_slots[ring_slot(j, S)].read = true;
+            }
+        }
+        if (spread)
+            CHECK(copy_a_before(ks, ks, la, lb, lead) == la && copy_b_before(ks, ks, la, lb, lead) == lb &&
+                      copy_a_before(0, ks, la, lb, lead) == 0 && copy_b_before(0, ks, la, lb, lead) == 0,
+                  "plan does not cover the tile");
+        wait_for(j + 1, ring_wait_steady(S, lead, la, lb));
+        // barrier
+        if (!spread) {
+            CHECK(ta == tb && ring_slot(ta, SA) == ring_slot(j, SA), "burst refills the freed slots");
+            issue_a(ta, 0, la);
+            issue_b(tb, 0, lb);
+        }
+    }
+    if (ring_fits_vmcnt(S, lead, la, lb))
+        CHECK(max_flight <= 63, "S=%d lead=%d la=%d lb=%d: %d copies in flight", S, lead, la, lb, max_flight);
+}
+
 void check_ring()
 {
+    const int loads[][2] = {{1, 1}, {2, 2}, {4, 4}, {8, 8}, {4, 8}, {8, 4}, {2, 6}, {3, 5}};
     for (int S = 2; S <= 10; ++S)
-        for (int nk = 0; nk <= 40; ++nk) {
-            int slot_tile[16];
-            bool slot_read[16];
-            for (int s = 0; s < 16; ++s) {
-                slot_tile[s] = -1;
-                slot_read[s] = true;
-            }
-            int issued = 0, real = 0;
-            auto issue = [&](int t) {
-                const int s = ring_slot(t, S);
-                // a slot holding a real tile is refilled only after it was read
-                CHECK(slot_tile[s] < 0 || slot_tile[s] >= nk || slot_read[s],
-                      "S=%d nk=%d: tile %d overwrites unread tile %d", S, nk, t, slot_tile[s]);
-                CHECK(t == issued, "S=%d nk=%d: tiles issued out of order (%d, expected %d)", S, nk, t, issued);
-                slot_tile[s] = t;
-                slot_read[s] = false;
-                ++issued;
-                real += t < nk;
-            };
-            // the wait for tile j is exact: it lets precisely the tiles issued
-            // after j stay in flight (copies complete in issue order)
-            auto wait_for = [&](int j, int allowed) {
-                CHECK(allowed == issued - 1 - j, "S=%d nk=%d: wait for tile %d allows %d, issued after it %d", S, nk,
-                      j, allowed, issued - 1 - j);
-                CHECK(slot_tile[ring_slot(j, S)] == j, "S=%d nk=%d: slot of tile %d holds %d", S, nk, j,
-                      slot_tile[ring_slot(j, S)]);
-            };
-            for (int t = 0; t < ring_prologue(S); ++t)
-                issue(t);
-            wait_for(0, ring_wait_first(S));
-            for (int j = 0; j < nk; ++j) {
-                CHECK(slot_tile[ring_slot(j, S)] == j, "S=%d nk=%d: tile %d not in its slot", S, nk, j);
-                if (ring_spread(S)) {
-                    // spread copies go out during iteration j, before its wait,
-                    // into the slot the previous barrier freed
-                    CHECK(ring_slot(ring_issue_tile(j, S), S) == ring_slot(j + S - 1, S), "spread slot");
-                    issue(ring_issue_tile(j, S));
-                }
-                slot_read[ring_slot(j, S)] = true;  // every LDS read of tile j has returned
-                wait_for(j + 1, ring_wait_steady(S));
-                // barrier
-                if (!ring_spread(S)) {
-                    CHECK(ring_slot(ring_issue_tile(j, S), S) == ring_slot(j, S), "burst refills the freed slot");
-                    issue(ring_issue_tile(j, S));
-                }
-            }
-            CHECK(real == nk, "S=%d nk=%d: %d real tiles issued", S, nk, real);
-        }
-    for (int loads = 1; loads <= 32; ++loads)
-        CHECK((ring_max_stages(loads) - 1) * loads <= 63 && ring_max_stages(loads) * loads > 63,
-              "ring_max_stages(%d)", loads);
+        for (int lead = 0; lead <= 1; ++lead)
+            for (auto &l : loads)
+                for (int ks = 2; ks <= 4; ks += 2)
+                    for (int nk = 0; nk <= 24; ++nk)
+                        check_ring_case(S, lead, l[0], l[1], ks, nk);
+    for (int n = 1; n <= 32; ++n)
+        CHECK((ring_max_stages(n) - 1) * n <= 63 && ring_max_stages(n) * n > 63, "ring_max_stages(%d)", n);
+    // the ring depths the kernel builds: B ring S, A ring S + lead
+    CHECK(ring_lds_bytes(2, 1, 32768, 32768) == 160 * 1024, "256x256x64 S=2 lead fills 160 KiB");
+    CHECK(ring_lds_bytes(3, 0, 16384, 16384) == 3 * 32768, "no-lead ring is S stages");
 }
 
 int main()

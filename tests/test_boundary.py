@@ -110,6 +110,27 @@ def test_unsupported_configurations():
     assert check(th=128, s=9) == pg.GEMM_ERR_UNSUPPORTED
 
 
+def test_leading_a_ring_budget_and_errors():
+    # S=2 plus one leading A tile: 256x256x64 fills 160 KiB exactly
+    assert pg.gemm_lds_bytes(256, 256, 64, 2, F16, a_lead=1) == 3 * 256 * 64 * 2 + 2 * 256 * 64 * 2 == MI355X
+    assert pg.gemm_lds_bytes(128, 256, 64, 2, F16, a_lead=1) == 3 * 128 * 64 * 2 + 2 * 256 * 64 * 2
+    assert pg.gemm_lds_bytes(128, 128, 32, 2, F16, a_lead=2) == -1
+    assert pg.gemm_check(NT, 4096, 4096, 4096, F16, 256, 256, 64, 2, 256, MI355X, a_lead=1) == pg.GEMM_OK
+    assert pg.gemm_check(NT, 4096, 4096, 4096, F16, 256, 256, 64, 2, 512, MI355X, a_lead=1) == pg.GEMM_OK
+    # 128x256x64: three stages are 144 KiB, plus a 16 KiB A tile = 160 KiB
+    assert pg.gemm_check(NT, 4096, 4096, 4096, F16, 128, 256, 64, 3, 256, MI355X, a_lead=1) == pg.GEMM_OK
+    # 256x128x64: three stages are 144 KiB, plus a 32 KiB A tile is over
+    assert pg.gemm_check(NT, 4096, 4096, 4096, F16, 256, 128, 64, 3, 256, MI355X, a_lead=1) == \
+        pg.GEMM_ERR_LDS_BUDGET
+    assert "leading" in pg.last_error()
+    assert pg.gemm_check(NT, 64, 64, 64, F16, 128, 128, 32, 1, 256, MI355X, a_lead=1) == pg.GEMM_ERR_ARG
+    assert pg.gemm_check(NT, 64, 64, 64, F16, 128, 128, 32, 0, 256, MI355X, a_lead=1) == pg.GEMM_ERR_ARG
+    assert pg.gemm_check(NT, 64, 64, 64, F16, 128, 128, 32, 3, 256, MI355X, a_lead=-1) == pg.GEMM_ERR_ARG
+    assert pg.gemm_check(NT, 64, 64, 64, F16, 128, 128, 32, 5, 256, MI355X, a_lead=1) == pg.GEMM_ERR_UNSUPPORTED
+    # against a larger budget a ring above 160 KiB passes the budget rule but has no kernel
+    assert pg.gemm_check(NT, 64, 64, 64, F16, 256, 256, 64, 3, 256, 228 * 1024) == pg.GEMM_ERR_UNSUPPORTED
+
+
 def test_zero_stages_is_the_single_buffer():
     assert check(s=0) == pg.GEMM_OK
     assert pg.gemm_lds_bytes(128, 128, 32, 0) == pg.gemm_lds_bytes(128, 128, 32, 1)
@@ -139,5 +160,6 @@ def test_no_device_reported_as_hip_error():
     assert pg.load().gemm_lds_budget() == -1
     assert check(budget=0) == pg.GEMM_ERR_HIP
     # launching entry points: bad arguments are still reported as such
-    assert pg.gemm_nt_raw(None, None, None, -1, 4, 8, F16, 128, 128, 32, 2, 256, None) == pg.GEMM_ERR_ARG
-    assert pg.gemm_nt_raw(16, 16, 16, 4, 4, 8, F16, 128, 128, 32, 2, 256, None) == pg.GEMM_ERR_HIP
+    assert pg.gemm_nt_raw(None, None, None, -1, 4, 8, F16, 128, 128, 32, 2, 0, 256, None) == pg.GEMM_ERR_ARG
+    assert pg.gemm_nt_raw(16, 16, 16, 4, 4, 8, F16, 128, 128, 32, 2, 0, 256, None) == pg.GEMM_ERR_HIP
+    assert pg.gemm_nt_raw(16, 16, 16, 4, 4, 8, F16, 128, 128, 32, 1, 1, 256, None) == pg.GEMM_ERR_ARG

@@ -32,10 +32,11 @@ def host(t):
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def run(layout, A, B, dtype, M, N, K, block, stages, threads, out=None):
+def run(layout, A, B, dtype, M, N, K, block, stages, threads, out=None, a_lead=0):
     dA, dB = dev(A, dtype), dev(B, dtype)
     fn = pg.gemm_nt if layout == "nt" else pg.gemm_nn
-    C = fn(dA.view(M, K), dB.view(B.shape), out=out, block=block, num_stages=stages, threads=threads)
+    C = fn(dA.view(M, K), dB.view(B.shape), out=out, block=block, num_stages=stages, threads=threads,
+           a_lead=a_lead)
     torch.cuda.synchronize()
     return host(C)
 
@@ -125,6 +126,19 @@ def test_nn_bf16_4096_over_budget_rejected():
     assert bool((out == 7.0).all()), "C was touched by a rejected call"
 
 
+@pytest.mark.parametrize("threads", [256, 512])
+def test_nt_f16_4096_leading_a_ring(oracle_gemm, threads):
+    # 256x256x64: two stages plus one leading A tile fill the 160 KiB exactly
+    w = inputs.workload("nt_f16_4096")
+    A, B = w.make()
+    rows = sample_rows(w.M, 256, 8)
+    want = oracle_rows(oracle_gemm, "nt", A, B, F16, rows)
+    got0 = run("nt", A, B, F16, w.M, w.N, w.K, (256, 256, 64), 2, threads)
+    got1 = run("nt", A, B, F16, w.M, w.N, w.K, (256, 256, 64), 2, threads, a_lead=1)
+    assert_close(got1[rows], want, F16, oracle_gemm, "4096^3 256x256x64 S=2 a_lead threads=%d" % threads)
+    assert np.array_equal(got0, got1), "a_lead changed the result"
+
+
 def test_ragged_4000x5000x3000(oracle_gemm):
     w = inputs.workload("nt_f16_ragged_4000x5000x3000")
     A, B = w.make()
@@ -140,13 +154,15 @@ def test_long_k_512x512x65536(oracle_gemm):
     rows = sample_rows(w.M, 128, 6, extra=4)
     want = oracle_rows(oracle_gemm, "nt", A, B, F16, rows)
     first = None
-    for s in (1, 2, 3, 4, 6):
-        got = run("nt", A, B, F16, w.M, w.N, w.K, (128, 128, 32), s, 256)
-        assert_close(got[rows], want, F16, oracle_gemm, "long K S=%d" % s)
+    for s, lead in ((1, 0), (2, 0), (3, 0), (4, 0), (6, 0), (2, 1), (3, 1), (4, 1)):
+        got = run("nt", A, B, F16, w.M, w.N, w.K, (128, 128, 32), s, 256, a_lead=lead)
+        assert_close(got[rows], want, F16, oracle_gemm, "long K S=%d a_lead=%d" % (s, lead))
         if first is None:
             first = got
         else:
             assert np.array_equal(got, first)
+    got = run("nt", A, B, F16, w.M, w.N, w.K, (256, 256, 64), 2, 512, a_lead=1)
+    assert_close(got[rows], want, F16, oracle_gemm, "long K 256x256x64 S=2 a_lead")
 
 
 # --------------------------------------------------------------------------
@@ -167,11 +183,17 @@ def test_every_tile_ragged(oracle_gemm, tile, layout, dtype):
     fn = oracle_gemm.gemm_nt if layout == "nt" else oracle_gemm.gemm_nn
     want = fn(A, B, dtype)
     budget = 160 * 1024
-    for s in (1, 2, 3):
-        if s * (bm + bn) * bk * 2 > budget:
+    first = None
+    for s, lead in ((1, 0), (2, 0), (3, 0), (2, 1), (3, 1)):
+        if (s * (bm + bn) + lead * bm) * bk * 2 > budget:
             continue
-        got = run(layout, A, B, dtype, M, N, K, (bm, bn, bk), s, th)
-        assert_close(got, want, dtype, oracle_gemm, "%s dtype=%d tile %s S=%d" % (layout, dtype, tile, s))
+        got = run(layout, A, B, dtype, M, N, K, (bm, bn, bk), s, th, a_lead=lead)
+        what = "%s dtype=%d tile %s S=%d a_lead=%d" % (layout, dtype, tile, s, lead)
+        assert_close(got, want, dtype, oracle_gemm, what)
+        if first is None:
+            first = got
+        else:
+            assert np.array_equal(got, first), what + " differs from S=1"
 
 
 # --------------------------------------------------------------------------
