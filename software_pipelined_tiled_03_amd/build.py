@@ -16,8 +16,9 @@ KERNEL_SRC = os.path.join(CSRC, "pipegemm_kernels.hip")
 HOST_SRC = os.path.join(CSRC, "pipegemm.hip")
 DEPS = [KERNEL_SRC, HOST_SRC, os.path.join(CSRC, "pipegemm_kernel.hpp"), os.path.join(CSRC, "pipegemm_launch.hpp"),
         os.path.join(ROOT, "include", "pipegemm.h")]
-# one kernel translation unit per (element type, B layout), compiled in parallel
-VARIANTS = [("f16_nt", "_Float16", 0), ("bf16_nt", "__bf16", 0), ("f16_nn", "_Float16", 1), ("bf16_nn", "__bf16", 1)]
+# one kernel translation unit per (element type, B layout, K bound), compiled in parallel
+VARIANTS = [("%s_%s_k%d" % (n, l, kc), e, nn, kc)
+            for n, e in (("f16", "_Float16"), ("bf16", "__bf16")) for l, nn in (("nt", 0), ("nn", 1)) for kc in (0, 1)]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -31,10 +32,10 @@ FLAGS = [
 
 def _compile_cmds(objdir, extra):
     cmds = []
-    for name, elem, nn in VARIANTS:
+    for name, elem, nn, kcheck in VARIANTS:
         obj = os.path.join(objdir, "kernels_%s.o" % name)
-        cmds.append((obj, [HIPCC, *FLAGS, *extra, "-DPG_ELEM=" + elem, "-DPG_NN=%d" % nn, "-c", KERNEL_SRC,
-                           "-o", obj]))
+        cmds.append((obj, [HIPCC, *FLAGS, *extra, "-DPG_ELEM=" + elem, "-DPG_NN=%d" % nn,
+                           "-DPG_KCHECK=%d" % kcheck, "-c", KERNEL_SRC, "-o", obj]))
     obj = os.path.join(objdir, "host.o")
     cmds.append((obj, [HIPCC, *FLAGS, *extra, "-c", HOST_SRC, "-o", obj]))
     return cmds

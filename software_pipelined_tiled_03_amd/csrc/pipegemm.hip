@@ -40,12 +40,12 @@ typedef hipError_t (*launch_fn)(const KernelArgs &, int grid, int lds_bytes, hip
 struct Instance {
     int dtype, layout, bm, bn, bk, threads;
     int a_loads, b_loads;  // 1 KiB copies per wave per K tile of A and of B (bound the vmcnt wait)
-    launch_fn launch;
+    launch_fn launch[2];   // [0]: K a multiple of block_K; [1]: ragged last K tile
 };
 
 #define PG_ROW(DT, T, LAYOUT, NN, BM, BN, BK, WM, WN)                                                  \
     {DT, LAYOUT, BM, BN, BK, 64 * WM * WN, loads_per_wave(BM, 0, BK, WM * WN), loads_per_wave(0, BN, BK, WM * WN), \
-     &launch<T, NN, BM, BN, BK, WM, WN>},
+     {&launch<T, NN, BM, BN, BK, WM, WN, false>, &launch<T, NN, BM, BN, BK, WM, WN, true>}},
 #define PG_ROW_F16_NT(BM, BN, BK, WM, WN) PG_ROW(GEMM_F16, _Float16, GEMM_NT, false, BM, BN, BK, WM, WN)
 #define PG_ROW_BF16_NT(BM, BN, BK, WM, WN) PG_ROW(GEMM_BF16, __bf16, GEMM_NT, false, BM, BN, BK, WM, WN)
 #define PG_ROW_F16_NN(BM, BN, BK, WM, WN) PG_ROW(GEMM_F16, _Float16, GEMM_NN, true, BM, BN, BK, WM, WN)
@@ -225,7 +225,7 @@ int run(int layout, const void *A, const void *B, void *C, int64_t M, int64_t N,
     if (grid >= (1LL << 31))
         return fail(GEMM_ERR_UNSUPPORTED, "too many tiles");
     const int lds = (int)lds_bytes_of(bm, bn, bk, a.stages, lead);
-    hipError_t e = in->launch(a, (int)grid, lds, (hipStream_t)stream);
+    hipError_t e = in->launch[K % bk != 0](a, (int)grid, lds, (hipStream_t)stream);
     if (e != hipSuccess)
         return fail(GEMM_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -283,7 +283,8 @@ __device__ __forceinline__ void sync_nn_operands(Frag (&fb)[FN])
 
 // ---------------------------------------------------------------------------
 // The kernel.
-template <class T, bool NN, class Cfg>
+// KCHECK: K is not a multiple of BK, so the last K tile is ragged.
+template <class T, bool NN, class Cfg, bool KCHECK>
 __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs p)
 {
     using E = Elem<T>;
@@ -302,22 +303,34 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
     const int m0 = tm * BM, n0 = tn * BN;
     const int K = p.K, N = p.N, nk = p.nk;
 
-    // Buffer resources: A panel rows m0.., B panel rows n0.. (NT) or columns n0.. (NN).
+    // The A panel (rows m0..) and the B panel (rows n0.. of the NT form, columns
+    // n0.. of the NN form), as byte ranges.  Each K tile is copied through a
+    // buffer resource of its panel shifted to the tile's first K position: a
+    // resource is four scalar registers, so the shift costs a few scalar
+    // instructions per tile and every lane's offset is the same in every tile.
+    // Bytes at or beyond the end of the panel read as zero, so in the NN form
+    // rows of B past K, and tiles past the end of K, land as zeros.  In the
+    // K-contiguous tiles a chunk past K in the ragged last tile would read the
+    // next row instead: with KCHECK those chunks get an out-of-range offset.
     const int a_rows = min(BM, p.M - m0);
-    const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)((const char *)p.A + (size_t)m0 * K * 2), 0, a_rows * K * 2, 0x00020000);
-    __amdgpu_buffer_rsrc_t rsB;
+    const char *const a_panel = (const char *)p.A + (size_t)m0 * K * 2;
+    const int a_bytes = a_rows * K * 2;
+    const char *b_panel;
+    int b_bytes;
     if constexpr (!NN) {
-        const int b_rows = min(BN, N - n0);
-        rsB = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)p.B + (size_t)n0 * K * 2), 0,
-                                                b_rows * K * 2, 0x00020000);
+        b_panel = (const char *)p.B + (size_t)n0 * K * 2;
+        b_bytes = min(BN, N - n0) * K * 2;
     } else {
-        rsB = __builtin_amdgcn_make_buffer_rsrc((void *)((const char *)p.B + (size_t)n0 * 2), 0,
-                                                (K * N - n0) * 2, 0x00020000);
+        b_panel = (const char *)p.B + (size_t)n0 * 2;
+        b_bytes = (K * N - n0) * 2;
     }
+    auto tile_rsrc = [](const char *panel, int bytes, int64_t shift) {
+        const int64_t left = (int64_t)bytes - shift;
+        return __builtin_amdgcn_make_buffer_rsrc((void *)(panel + shift), 0, left > 0 ? (int)left : 0, 0x00020000);
+    };
 
-    // Per-lane source offsets of this wave's copies (relative to K tile 0) and
-    // the K position of each chunk within a tile (for the K bound).
+    // Per-lane source offsets of this wave's copies within a tile and the K
+    // position of each chunk within a tile (for the K bound).
     uint32_t a_off[Cfg::A_LOADS];
     int a_kc[Cfg::A_LOADS];
 #pragma unroll
@@ -341,35 +354,37 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
             int k, c;
             n_tile_unit<BN>(u, k, c);
             b_off[t] = (n0 + c * 8 < N) ? (uint32_t)(k * N * 2 + c * 16) : kOOB;
-            b_kc[t] = k;
+            b_kc[t] = 0;
         }
     }
 
     // Issue this wave's copies [first, last) of the A tile (B tile) of K tile
-    // kt into the slot at `dst`.  Chunks at or beyond K (the ragged last tile,
-    // or a tile past the end of K) get an out-of-range offset and land as zeros.
+    // kt into the slot at `dst`.
     auto issue_a = [&](int kt, char *dst, int first, int last) {
         const int kbase = kt * BK;
+        const __amdgpu_buffer_rsrc_t rs = tile_rsrc(a_panel, a_bytes, (int64_t)kbase * 2);
 #pragma unroll
         for (int t = 0; t < Cfg::A_LOADS; ++t) {
             if (t < first || t >= last)
                 continue;
-            const uint32_t off = kbase + a_kc[t] < K ? a_off[t] + (uint32_t)kbase * 2 : kOOB;
-            copy_1k(rsA, dst + (t * WAVES + wave) * 1024, off);
+            uint32_t off = a_off[t];
+            if constexpr (KCHECK)
+                off = kbase + a_kc[t] < K ? off : kOOB;
+            copy_1k(rs, dst + (t * WAVES + wave) * 1024, off);
         }
     };
     auto issue_b = [&](int kt, char *dst, int first, int last) {
         const int kbase = kt * BK;
+        const __amdgpu_buffer_rsrc_t rs =
+            tile_rsrc(b_panel, b_bytes, NN ? (int64_t)kbase * N * 2 : (int64_t)kbase * 2);
 #pragma unroll
         for (int t = 0; t < Cfg::B_LOADS; ++t) {
             if (t < first || t >= last)
                 continue;
-            uint32_t off;
-            if constexpr (!NN)
-                off = kbase + b_kc[t] < K ? b_off[t] + (uint32_t)kbase * 2 : kOOB;
-            else
-                off = kbase + b_kc[t] < K && b_off[t] != kOOB ? b_off[t] + (uint32_t)kbase * N * 2 : kOOB;
-            copy_1k(rsB, dst + (t * WAVES + wave) * 1024, off);
+            uint32_t off = b_off[t];
+            if constexpr (KCHECK && !NN)
+                off = kbase + b_kc[t] < K ? off : kOOB;
+            copy_1k(rs, dst + (t * WAVES + wave) * 1024, off);
         }
     };
 

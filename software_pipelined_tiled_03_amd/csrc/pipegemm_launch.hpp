@@ -12,9 +12,10 @@ struct KernelArgs;
 // 128 x 128 x 32 (16 KiB), so no deeper ring fits gfx950's 160 KiB anyway.
 constexpr int kMaxStages = 10;
 
-// Launch gemm_kernel<T, NN, Tile<BM, BN, BK, WM, WN>> on `stream` with `grid`
-// workgroups and `lds_bytes` of dynamic LDS.
-template <class T, bool NN, int BM, int BN, int BK, int WM, int WN>
+// Launch gemm_kernel<T, NN, Tile<BM, BN, BK, WM, WN>, KCHECK> on `stream` with
+// `grid` workgroups and `lds_bytes` of dynamic LDS.  KCHECK: K is not a
+// multiple of BK.
+template <class T, bool NN, int BM, int BN, int BK, int WM, int WN, bool KCHECK>
 hipError_t launch(const KernelArgs &args, int grid, int lds_bytes, hipStream_t stream);
 
 // 1 KiB copies each wave issues per K tile (bounds the copy wait, 63 loads);
