@@ -2,10 +2,12 @@
 
 A step is one GEMM call, C = A[M,K] . B^T, on inputs already resident in
 HBM.  The headline workload is the 4096^3 fp16 NT GEMM; `value` is its
-throughput in TFLOP/s (2MNK / t).  The line also carries the num_stages sweep
-of the 128x128x32 tile (the pages' default) and of the headline tile, the
-roofline of the kernel (MFMA bound, measured with HIP events on the launch
-stream), and the CPU oracle timed on a bounded row sample of the same GEMM.
+throughput in TFLOP/s (2MNK / t) with the fastest configuration (256x256x64
+tile, two stages plus a leading A tile, 4 waves).  The line also carries the
+num_stages sweep of the 128x128x32 tile (the tutorial's default) and of the
+256x256 tiles, the roofline of the kernel (MFMA bound, measured with HIP
+events on the launch stream), and the CPU oracle timed on a bounded row
+sample of the same GEMM.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-cpu-baseline]
 """
@@ -20,17 +22,22 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA, published
-HEADLINE = dict(workload="nt_f16_4096", block=(256, 256, 32), num_stages=3, threads=512)
+HEADLINE = dict(workload="nt_f16_4096", block=(256, 256, 64), num_stages=2, a_lead=1, threads=256)
+# (label, workload, block, threads, ring depths); a depth "S+A" is num_stages S with a_lead = 1
 SWEEPS = [
-    # (label, workload, block, threads, stages)
-    ("tile128x128x32_t256", "nt_f16_4096", (128, 128, 32), 256, (1, 2, 3, 4, 6)),
-    ("tile256x256x32_t512", "nt_f16_4096", (256, 256, 32), 512, (1, 2, 3, 4, 5)),
-    ("tile256x256x32_t256", "nt_f16_4096", (256, 256, 32), 256, (1, 2, 3, 4, 5)),
-    ("tile256x256x64_t512", "nt_f16_4096", (256, 256, 64), 512, (1, 2)),
-    ("nn_bf16_tile128x128x32_t256", "nn_bf16_4096", (128, 128, 32), 256, (3,)),
-    ("nn_bf16_tile128x256x64_t256", "nn_bf16_4096", (128, 256, 64), 256, (3,)),
-    ("nn_bf16_tile256x128x32_t256", "nn_bf16_4096", (256, 128, 32), 256, (3,)),
+    ("tile128x128x32_t256", "nt_f16_4096", (128, 128, 32), 256, ("1", "2", "3", "4", "6")),
+    ("tile256x256x32_t256", "nt_f16_4096", (256, 256, 32), 256, ("1", "2", "3", "4", "5", "2+A", "3+A")),
+    ("tile256x256x64_t256", "nt_f16_4096", (256, 256, 64), 256, ("1", "2", "2+A")),
+    ("tile256x256x64_t512", "nt_f16_4096", (256, 256, 64), 512, ("1", "2", "2+A")),
+    ("nn_bf16_tile128x128x32_t256", "nn_bf16_4096", (128, 128, 32), 256, ("3",)),
+    ("nn_bf16_tile256x256x64_t256", "nn_bf16_4096", (256, 256, 64), 256, ("2", "2+A")),
 ]
+
+
+def parse_depth(d):
+    """'3' -> (3, 0); '2+A' -> (2, 1)."""
+    d = str(d)
+    return (int(d[:-2]), 1) if d.endswith("+A") else (int(d), 0)
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -46,13 +53,13 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-def measured_traffic(block, stages, threads):
+def measured_traffic(block, stages, a_lead, threads):
     """HBM bytes per launch from a committed rocprofv3 summary of this exact
     kernel configuration, or None if there is none or the kernel sources
     changed since it was taken.  The summary carries lines
-    `config: <BMxBNxBK> S=<s> threads=<t>`, `source_sha256: <hex>` and
+    `config: <BMxBNxBK> S=<s>[+A] threads=<t>`, `source_sha256: <hex>` and
     `hbm_bytes_per_launch: <int>`."""
-    want = "%dx%dx%d S=%d threads=%d" % (block[0], block[1], block[2], stages, threads)
+    want = "%dx%dx%d S=%d%s threads=%d" % (block[0], block[1], block[2], stages, "+A" if a_lead else "", threads)
     src = kernel_source_hash()
     if not os.path.isdir(PROFILES):
         return None
@@ -87,19 +94,19 @@ def _device_inputs(w):
     return A, B, dA, dB
 
 
-def time_gemm(fn, dA, dB, C, block, stages, threads, steps, warmup):
+def time_gemm(fn, dA, dB, C, block, stages, threads, steps, warmup, a_lead=0):
     """Average milliseconds per call over `steps` back-to-back launches."""
     import torch
 
     for _ in range(warmup):
-        fn(dA, dB, out=C, block=block, num_stages=stages, threads=threads)
+        fn(dA, dB, out=C, block=block, num_stages=stages, threads=threads, a_lead=a_lead)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for _ in range(steps):
-        fn(dA, dB, out=C, block=block, num_stages=stages, threads=threads)
+        fn(dA, dB, out=C, block=block, num_stages=stages, threads=threads, a_lead=a_lead)
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
@@ -131,7 +138,7 @@ def main():
     ap.add_argument("--no-context", action="store_true", help="skip the torch.matmul context timing")
     ap.add_argument("--workload", default=HEADLINE["workload"], help="one of inputs.WORKLOADS")
     ap.add_argument("--block", default=None, help="tile as BMxBNxBK (default: the headline tile)")
-    ap.add_argument("--stages", type=int, default=None)
+    ap.add_argument("--stages", default=None, help="ring depth, e.g. 3 or 2+A (num_stages 2 with a_lead)")
     ap.add_argument("--threads", type=int, default=None)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
@@ -180,12 +187,13 @@ def main():
             sA, sB, sC, sfn = operands[wl]
             sflops = 2.0 * sA.shape[0] * sC.shape[1] * sA.shape[1]
             row = {}
-            for s in stages:
-                ms = time_gemm(sfn, sA, sB, sC, block, s, th, steps=30, warmup=5)
-                row[str(s)] = dict(tflops=round(sflops / ms / 1e9, 1),
-                                   pct_peak=round(100 * sflops / ms / 1e9 / PEAK_TFLOPS, 1),
-                                   lds_bytes=pg.gemm_lds_bytes(block[0], block[1], block[2], s))
-                _log("sweep %s S=%d: %.1f TFLOP/s" % (label, s, sflops / ms / 1e9))
+            for d in stages:
+                s, lead = parse_depth(d)
+                ms = time_gemm(sfn, sA, sB, sC, block, s, th, steps=30, warmup=5, a_lead=lead)
+                row[d] = dict(tflops=round(sflops / ms / 1e9, 1),
+                              pct_peak=round(100 * sflops / ms / 1e9 / PEAK_TFLOPS, 1),
+                              lds_bytes=pg.gemm_lds_bytes(block[0], block[1], block[2], s, a_lead=lead))
+                _log("sweep %s S=%s: %.1f TFLOP/s" % (label, d, sflops / ms / 1e9))
             sweep[label] = row
         rej = None
         nA, nB, nC, nfn = operands.get("nn_bf16_4096", (None, None, None, None))
@@ -198,11 +206,15 @@ def main():
         del operands
 
     block = tuple(int(x) for x in args.block.split("x")) if args.block else HEADLINE["block"]
-    stages = args.stages if args.stages is not None else HEADLINE["num_stages"]
+    if args.stages is not None:
+        stages, a_lead = parse_depth(args.stages)
+    else:
+        stages, a_lead = HEADLINE["num_stages"], HEADLINE["a_lead"]
     threads = args.threads if args.threads is not None else HEADLINE["threads"]
-    ms = time_gemm(fn, dA, dB, C, block, stages, threads, steps=args.steps, warmup=args.warmup)
+    ms = time_gemm(fn, dA, dB, C, block, stages, threads, steps=args.steps, warmup=args.warmup, a_lead=a_lead)
     tflops = flops / ms / 1e9
-    _log("headline %s tile %s S=%d threads=%d: %.3f ms, %.1f TFLOP/s" % (w.name, block, stages, threads, ms, tflops))
+    _log("headline %s tile %s S=%d%s threads=%d: %.3f ms, %.1f TFLOP/s"
+         % (w.name, block, stages, "+A" if a_lead else "", threads, ms, tflops))
 
     # context: the vendor library on the same operands
     ref = None
@@ -243,10 +255,11 @@ def main():
         "config": {"workload": "GEMM %s %dx%dx%d %s, fp32 accumulate" % (
                        w.layout.upper(), w.M, w.N, w.K, "fp16 uniform[-1,1]" if w.dtype == inputs.F16 else "bf16 normal(0,1)"),
                    "M": w.M, "N": w.N, "K": w.K, "layout": w.layout.upper(), "block": list(block),
-                   "num_stages": stages, "threads": threads},
+                   "num_stages": stages, "a_lead": a_lead, "threads": threads},
         "pct_peak": round(100 * tflops / PEAK_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(tflops / PEAK_TFLOPS, 4), "traffic": measured_traffic(block, stages, threads)},
+                     "frac": round(tflops / PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic(block, stages, a_lead, threads)},
         "cpu_baseline": cpu,
         "per_num_stages": sweep,
         "context_torch_matmul_tflops": ref,
