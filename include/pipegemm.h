@@ -143,6 +143,69 @@ int gemm_check(int layout, int64_t M, int64_t N, int64_t K, int dtype, int block
                int block_K, int num_stages, int a_lead, int threads, int64_t lds_budget);
 
 /*
+ * Tuning (TileLang tutorial, chapter 11, sections 3.5-3.8: a configuration
+ * space given per problem, pre-pruned of tiles that do not divide the problem
+ * and of over-budget combinations, every candidate measured on the same
+ * operands, and the result fixed as a per-device default).
+ *
+ * gemm_config: the tuned parameters of gemm_nt / gemm_nn.
+ */
+typedef struct gemm_config {
+    int32_t block_M, block_N, block_K;
+    int32_t num_stages;
+    int32_t a_lead;
+    int32_t threads;
+} gemm_config;
+
+/* gemm_prune status of a candidate whose tile does not divide M, N or K */
+#define GEMM_PRUNE_NODIV 16
+
+/*
+ * gemm_configs: the built configuration space for (layout, dtype): every tile
+ * and thread count with a kernel, with every ring depth the kernel is built
+ * for (num_stages 1..10, a_lead 0 or 1) whose LDS fits 160 KiB.  Writes up to
+ * `max` entries to `out` (out may be NULL when max is 0) and returns the total
+ * number, or -1 for an unknown layout or dtype.  Pure host.
+ */
+int gemm_configs(int layout, int dtype, gemm_config *out, int max);
+
+/*
+ * gemm_prune: pre-pruning (chapter 11, section 3.7).  For each of the n
+ * candidates writes status[i]: GEMM_PRUNE_NODIV if its tile does not divide
+ * M, N and K, otherwise what gemm_check returns for it against lds_budget
+ * (0 = the current device's).  Returns the number of candidates left with
+ * GEMM_OK, or -1 for bad arguments.  Pure host when lds_budget > 0.
+ */
+int gemm_prune(int layout, int64_t M, int64_t N, int64_t K, int dtype, const gemm_config *cands, int n,
+               int64_t lds_budget, int *status);
+
+/*
+ * gemm_tune: measures every candidate whose status[i] is GEMM_OK on the same
+ * operands (chapter 11, sections 3.5-3.6): `warmup` launches, then `reps`
+ * launches timed together with HIP events on hip_stream.  Writes the mean
+ * milliseconds per launch to ms[i] (-1 for skipped candidates) and the index
+ * of the fastest to *best (-1 if none ran).  A, B, C and the sizes are as for
+ * gemm_nt / gemm_nn (layout selects which); every candidate writes the same C,
+ * because the accumulation order over K does not depend on the configuration.
+ * Synchronous: returns after the last timed launch has finished.  Returns
+ * GEMM_OK or the status of the first failing launch (then the remaining ms[i]
+ * are not written).
+ */
+int gemm_tune(int layout, const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype,
+              const gemm_config *cands, const int *status, int n, int warmup, int reps, void *hip_stream,
+              float *ms, int *best);
+
+/*
+ * gemm_default_config: the configuration this library picks for a problem on
+ * gfx950 without tuning (chapter 11, section 3.8: fix the tuned result as a
+ * per-device default): the largest tile whose grid fills the 256 compute
+ * units, with the fastest ring measured for that tile, else the tile with the
+ * most workgroups (8 waves instead of 4 for the 256 x 256 tile when
+ * K <= 1024).  Pure host.  Returns GEMM_OK or GEMM_ERR_ARG.
+ */
+int gemm_default_config(int layout, int64_t M, int64_t N, int64_t K, int dtype, gemm_config *out);
+
+/*
  * gemm_last_error: message describing the last non-OK status returned on
  * this thread ("" if none).  The string is owned by the library and stays
  * valid until the next call on this thread.

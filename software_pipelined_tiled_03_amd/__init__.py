@@ -1,14 +1,16 @@
 """MI355X-native software-pipelined tiled half-precision GEMM.
 
 The compute path is the HIP library built from csrc/ (C-ABI in
-include/pipegemm.h); this package is its binding plus the seeded synthetic
-input generator (inputs.py).  Importing the package does not load the
+include/pipegemm.h); this package is its binding, the tuning front end
+(tuning.py) and the seeded synthetic input generator (inputs.py).  Importing the package does not load the
 library; the first call does, and raises if it has not been built.
 """
 from .binding import (GEMM_BF16, GEMM_F16, GEMM_NN, GEMM_NT, AlignmentError, GemmArgumentError, GemmError,
                       GemmHipError, LdsBudgetError, UnsupportedConfigError, gemm_check, gemm_lds_budget,
                       gemm_lds_bytes, gemm_nn, gemm_nn_raw, gemm_nt, gemm_nt_raw, last_error, load)
+from .tuning import TuneResult, TuningSpaceError, built_configs, default_config, matmul, plan, prune, tune
 
 __all__ = ["GEMM_BF16", "GEMM_F16", "GEMM_NN", "GEMM_NT", "AlignmentError", "GemmArgumentError", "GemmError",
            "GemmHipError", "LdsBudgetError", "UnsupportedConfigError", "gemm_check", "gemm_lds_budget",
-           "gemm_lds_bytes", "gemm_nn", "gemm_nn_raw", "gemm_nt", "gemm_nt_raw", "last_error", "load"]
+           "gemm_lds_bytes", "gemm_nn", "gemm_nn_raw", "gemm_nt", "gemm_nt_raw", "last_error", "load",
+           "TuneResult", "TuningSpaceError", "built_configs", "default_config", "matmul", "plan", "prune", "tune"]

@@ -231,10 +231,172 @@ int run(int layout, const void *A, const void *B, void *C, int64_t M, int64_t N,
     return ok();
 }
 
+// ---------------------------------------------------------------------------
+// Configuration space, pre-pruning, tuning and the gfx950 default table.
+
+// Every built (tile, threads) with every ring the kernel builds for it, in
+// table order, then S ascending, a_lead 0 before 1.
+int enumerate_configs(int layout, int dtype, gemm_config *out, int max)
+{
+    int n = 0;
+    for (const Instance &in : kInstances) {
+        if (in.layout != layout || in.dtype != dtype)
+            continue;
+        for (int s = 1; s <= kMaxStages; ++s)
+            for (int lead = 0; lead <= 1; ++lead) {
+                if (lead && (s < 2 || s > kMaxLeadStages))
+                    continue;
+                if (!ring_fits_vmcnt(s, lead, in.a_loads, in.b_loads) ||
+                    lds_bytes_of(in.bm, in.bn, in.bk, s, lead) > 160 * 1024)
+                    continue;
+                if (out && n < max)
+                    out[n] = gemm_config{in.bm, in.bn, in.bk, s, lead, in.threads};
+                ++n;
+            }
+    }
+    return n;
+}
+
+int64_t tiles_of(int64_t M, int64_t N, int bm, int bn)
+{
+    return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+}
+
 }  // namespace
 }  // namespace pipegemm
 
 extern "C" {
+
+int gemm_configs(int layout, int dtype, gemm_config *out, int max)
+{
+    if ((layout != GEMM_NT && layout != GEMM_NN) || (dtype != GEMM_F16 && dtype != GEMM_BF16) || max < 0 ||
+        (out == nullptr && max > 0))
+        return pipegemm::fail(GEMM_ERR_ARG, "gemm_configs: bad layout, dtype or output array"), -1;
+    pipegemm::ok();
+    return pipegemm::enumerate_configs(layout, dtype, out, max);
+}
+
+int gemm_prune(int layout, int64_t M, int64_t N, int64_t K, int dtype, const gemm_config *cands, int n,
+               int64_t lds_budget, int *status)
+{
+    if (n < 0 || (n > 0 && (cands == nullptr || status == nullptr)))
+        return pipegemm::fail(GEMM_ERR_ARG, "gemm_prune: bad candidate array"), -1;
+    int64_t budget = lds_budget;
+    if (budget == 0 && pipegemm::device_budget(&budget) != GEMM_OK)
+        return -1;
+    int legal = 0;
+    for (int i = 0; i < n; ++i) {
+        const gemm_config &c = cands[i];
+        // first: tiles that do not divide the problem
+        if (c.block_M <= 0 || c.block_N <= 0 || c.block_K <= 0) {
+            status[i] = GEMM_ERR_ARG;
+            continue;
+        }
+        if (M % c.block_M || N % c.block_N || K % c.block_K) {
+            status[i] = GEMM_PRUNE_NODIV;
+            continue;
+        }
+        // then: the launch-time validation (budget first, then the rest)
+        status[i] = pipegemm::validate(layout, M, N, K, dtype, c.block_M, c.block_N, c.block_K, c.num_stages,
+                                       c.a_lead, c.threads, budget, nullptr, nullptr);
+        legal += status[i] == GEMM_OK;
+    }
+    pipegemm::ok();
+    return legal;
+}
+
+int gemm_tune(int layout, const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype,
+              const gemm_config *cands, const int *status, int n, int warmup, int reps, void *hip_stream, float *ms,
+              int *best)
+{
+    if (n < 0 || (n > 0 && (cands == nullptr || status == nullptr || ms == nullptr)) || best == nullptr ||
+        warmup < 0 || reps < 1)
+        return pipegemm::fail(GEMM_ERR_ARG, "gemm_tune: bad arguments");
+    *best = -1;
+    hipStream_t stream = (hipStream_t)hip_stream;
+    hipEvent_t t0 = nullptr, t1 = nullptr;
+    hipError_t e = hipEventCreate(&t0);
+    if (e == hipSuccess)
+        e = hipEventCreate(&t1);
+    if (e != hipSuccess) {
+        if (t0)
+            (void)hipEventDestroy(t0);
+        return pipegemm::fail(GEMM_ERR_HIP, "hipEventCreate: %s", hipGetErrorString(e));
+    }
+    int st = GEMM_OK;
+    float best_ms = 0.f;
+    for (int i = 0; i < n && st == GEMM_OK; ++i) {
+        ms[i] = -1.f;
+        if (status[i] != GEMM_OK)
+            continue;
+        const gemm_config &c = cands[i];
+        auto launch = [&] {
+            return pipegemm::run(layout, A, B, C, M, N, K, dtype, c.block_M, c.block_N, c.block_K, c.num_stages,
+                                 c.a_lead, c.threads, hip_stream);
+        };
+        for (int w = 0; w < warmup && st == GEMM_OK; ++w)
+            st = launch();
+        if (st == GEMM_OK && (e = hipEventRecord(t0, stream)) != hipSuccess)
+            st = pipegemm::fail(GEMM_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+        for (int r = 0; r < reps && st == GEMM_OK; ++r)
+            st = launch();
+        if (st == GEMM_OK && (e = hipEventRecord(t1, stream)) != hipSuccess)
+            st = pipegemm::fail(GEMM_ERR_HIP, "hipEventRecord: %s", hipGetErrorString(e));
+        if (st == GEMM_OK && (e = hipEventSynchronize(t1)) != hipSuccess)
+            st = pipegemm::fail(GEMM_ERR_HIP, "hipEventSynchronize: %s", hipGetErrorString(e));
+        float t = 0.f;
+        if (st == GEMM_OK && (e = hipEventElapsedTime(&t, t0, t1)) != hipSuccess)
+            st = pipegemm::fail(GEMM_ERR_HIP, "hipEventElapsedTime: %s", hipGetErrorString(e));
+        if (st != GEMM_OK)
+            break;
+        ms[i] = t / reps;
+        if (*best < 0 || ms[i] < best_ms) {
+            *best = i;
+            best_ms = ms[i];
+        }
+    }
+    (void)hipEventDestroy(t0);
+    (void)hipEventDestroy(t1);
+    if (st == GEMM_OK)
+        pipegemm::ok();
+    return st;
+}
+
+int gemm_default_config(int layout, int64_t M, int64_t N, int64_t K, int dtype, gemm_config *out)
+{
+    if ((layout != GEMM_NT && layout != GEMM_NN) || (dtype != GEMM_F16 && dtype != GEMM_BF16) || M < 0 || N < 0 ||
+        K < 0 || out == nullptr)
+        return pipegemm::fail(GEMM_ERR_ARG, "gemm_default_config: bad arguments");
+    // Largest tile first; the first whose grid fills the 256 CUs wins, else the
+    // one with the most workgroups.  The ring of each tile is its fastest
+    // measured one on MI355X (256x256x64: two stages + leading A).  Tuning the
+    // built space on seven shapes from 1024x1024x8192 to 16384x4096x4096 puts
+    // this choice within 1 % of the winner, except that for K <= 1024 the
+    // 256x256x64 tile is faster with 8 waves (5 % at 4096x4096x512).
+    static const gemm_config kTable[] = {
+        {256, 256, 64, 2, 1, 256},
+        {256, 128, 64, 3, 0, 256},
+        {128, 256, 64, 3, 1, 256},
+        {128, 128, 64, 4, 0, 256},
+    };
+    const gemm_config *pick = nullptr;
+    int64_t most = -1;
+    for (const gemm_config &c : kTable) {
+        const int64_t t = pipegemm::tiles_of(M, N, c.block_M, c.block_N);
+        if (t >= 256) {
+            pick = &c;
+            break;
+        }
+        if (t > most) {
+            most = t;
+            pick = &c;
+        }
+    }
+    *out = *pick;
+    if (out->block_M == 256 && out->block_N == 256 && K <= 1024)
+        out->threads = 512;
+    return pipegemm::ok();
+}
 
 int gemm_nt(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype, int block_M,
             int block_N, int block_K, int num_stages, int a_lead, int threads, void *hip_stream)
