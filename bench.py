@@ -41,13 +41,19 @@ def parse_depth(d):
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+KERNEL_SOURCES = ("pipegemm_kernel.hpp", "pipegemm_kernels.hip", "pipegemm_launch.hpp", "pipegemm_layout.hpp")
+
+
 def kernel_source_hash():
-    """sha256 of the HIP sources and headers the kernels are built from."""
+    """sha256 of the device-code sources the kernels are built from (the
+    kernel template, its layouts and schedule, and its instantiations; the
+    host-side validation and tuning code does not change what a launch
+    moves)."""
     import hashlib
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "software_pipelined_tiled_03_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
