@@ -100,19 +100,19 @@ def _device_inputs(w):
     return A, B, dA, dB
 
 
-def time_gemm(fn, dA, dB, C, block, stages, threads, steps, warmup, a_lead=0):
+def time_gemm(fn, dA, dB, C, block, stages, threads, steps, warmup, a_lead=0, relu=False):
     """Average milliseconds per call over `steps` back-to-back launches."""
     import torch
 
     for _ in range(warmup):
-        fn(dA, dB, out=C, block=block, num_stages=stages, threads=threads, a_lead=a_lead)
+        fn(dA, dB, out=C, block=block, num_stages=stages, threads=threads, a_lead=a_lead, relu=relu)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for _ in range(steps):
-        fn(dA, dB, out=C, block=block, num_stages=stages, threads=threads, a_lead=a_lead)
+        fn(dA, dB, out=C, block=block, num_stages=stages, threads=threads, a_lead=a_lead, relu=relu)
     end.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
@@ -222,6 +222,11 @@ def main():
     _log("headline %s tile %s S=%d%s threads=%d: %.3f ms, %.1f TFLOP/s"
          % (w.name, block, stages, "+A" if a_lead else "", threads, ms, tflops))
 
+    # the fused GEMM+ReLU epilogue in the same configuration
+    relu_ms = time_gemm(fn, dA, dB, C, block, stages, threads, steps=max(10, args.steps // 2), warmup=args.warmup,
+                        a_lead=a_lead, relu=True)
+    _log("headline with fused ReLU: %.3f ms, %.1f TFLOP/s" % (relu_ms, flops / relu_ms / 1e9))
+
     # context: the vendor library on the same operands
     ref = None
     try:
@@ -268,6 +273,7 @@ def main():
                      "traffic": measured_traffic(block, stages, a_lead, threads)},
         "cpu_baseline": cpu,
         "per_num_stages": sweep,
+        "fused_relu": {"tflops": round(flops / relu_ms / 1e9, 2), "ms_per_step": round(relu_ms, 5)},
         "context_torch_matmul_tflops": ref,
     }
     print(json.dumps(out), flush=True)

@@ -113,6 +113,20 @@ int gemm_nn(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t
             int block_M, int block_N, int block_K, int num_stages, int a_lead, int threads, void *hip_stream);
 
 /*
+ * gemm_nt_relu, gemm_nn_relu: C = relu(A . B) with the ReLU fused into the
+ * store of C: each fp32 sum s becomes (s > 0 ? s : +0) before it is rounded to
+ * the input dtype (a NaN sum gives +0).
+ *
+ * Defined by: TileLang tutorial, chapter 11, section 4.6 (the GEMM+ReLU
+ * example on the same pipelined K loop).  Arguments, layouts, validation and
+ * errors exactly as gemm_nt / gemm_nn.
+ */
+int gemm_nt_relu(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype,
+                 int block_M, int block_N, int block_K, int num_stages, int a_lead, int threads, void *hip_stream);
+int gemm_nn_relu(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype,
+                 int block_M, int block_N, int block_K, int num_stages, int a_lead, int threads, void *hip_stream);
+
+/*
  * gemm_lds_bytes: LDS the pipeline of one workgroup needs,
  *   max(num_stages, 1) x (block_M x block_K + block_K x block_N) x 2 bytes,
  *   plus block_M x block_K x 2 bytes when a_lead is 1.

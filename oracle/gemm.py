@@ -46,10 +46,10 @@ def _load():
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_gemm_rows.argtypes = [u16p, u16p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
                                          ctypes.c_int64, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
-                                         u16p, f32p, i64p]
+                                         ctypes.c_int, u16p, f32p, i64p]
         lib.oracle_gemm_rows.restype = ctypes.c_int
         lib.oracle_gemm_points.argtypes = [u16p, u16p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64,
-                                           ctypes.c_int64, ctypes.c_int, i64p, i64p, ctypes.c_int64,
+                                           ctypes.c_int64, ctypes.c_int, ctypes.c_int, i64p, i64p, ctypes.c_int64,
                                            u16p, f32p]
         lib.oracle_gemm_points.restype = ctypes.c_int
         _lib = lib
@@ -88,7 +88,7 @@ def encode(values, dtype: int) -> np.ndarray:
     return out
 
 
-def _gemm_rows(A, B, b_layout, M, N, K, dtype, m_begin, m_end, want_sums):
+def _gemm_rows(A, B, b_layout, M, N, K, dtype, m_begin, m_end, want_sums, relu=False):
     A = _u16(A)
     B = _u16(B)
     if A.size != M * K or B.size != N * K:
@@ -98,17 +98,19 @@ def _gemm_rows(A, B, b_layout, M, N, K, dtype, m_begin, m_end, want_sums):
     S = np.empty((rows, N), dtype=np.float32) if want_sums else None
     cnt = ctypes.c_int64(0)
     rc = _load().oracle_gemm_rows(_ptr(A, ctypes.c_uint16), _ptr(B, ctypes.c_uint16), b_layout,
-                                  M, N, K, dtype, m_begin, m_end, _ptr(C, ctypes.c_uint16),
+                                  M, N, K, dtype, m_begin, m_end, int(bool(relu)), _ptr(C, ctypes.c_uint16),
                                   _ptr(S, ctypes.c_float) if want_sums else None, ctypes.byref(cnt))
     if rc != 0:
         raise ValueError("oracle_gemm_rows rejected its arguments")
     return C, S, cnt.value
 
 
-def gemm_nt(A, B, dtype: int, rows=None, return_sums=False, return_count=False):
+def gemm_nt(A, B, dtype: int, rows=None, return_sums=False, return_count=False, relu=False):
     """C = round(A[M,K] . B[N,K]^T) with ascending-k binary32 accumulation.
 
     rows=(m_begin, m_end) restricts the computation to those rows of C.
+    relu=True applies the ReLU epilogue (s > 0 ? s : +0) to each binary32 sum
+    before the rounding (TileLang tutorial, chapter 11, section 4.6).
     Returns C (and, on request, the binary32 sums and the multiply-add count).
     """
     M, K = A.shape
@@ -116,7 +118,7 @@ def gemm_nt(A, B, dtype: int, rows=None, return_sums=False, return_count=False):
     if K != K2:
         raise ValueError("inner dimensions differ")
     m0, m1 = rows if rows is not None else (0, M)
-    C, S, cnt = _gemm_rows(A, B, _B_NK, M, N, K, dtype, m0, m1, return_sums)
+    C, S, cnt = _gemm_rows(A, B, _B_NK, M, N, K, dtype, m0, m1, return_sums, relu)
     out = (C,)
     if return_sums:
         out += (S,)
@@ -125,14 +127,15 @@ def gemm_nt(A, B, dtype: int, rows=None, return_sums=False, return_count=False):
     return out[0] if len(out) == 1 else out
 
 
-def gemm_nn(A, B, dtype: int, rows=None, return_sums=False, return_count=False):
-    """C = round(A[M,K] . B[K,N]) with ascending-k binary32 accumulation."""
+def gemm_nn(A, B, dtype: int, rows=None, return_sums=False, return_count=False, relu=False):
+    """C = round(A[M,K] . B[K,N]) with ascending-k binary32 accumulation
+    (relu as for gemm_nt)."""
     M, K = A.shape
     K2, N = B.shape
     if K != K2:
         raise ValueError("inner dimensions differ")
     m0, m1 = rows if rows is not None else (0, M)
-    C, S, cnt = _gemm_rows(A, B, _B_KN, M, N, K, dtype, m0, m1, return_sums)
+    C, S, cnt = _gemm_rows(A, B, _B_KN, M, N, K, dtype, m0, m1, return_sums, relu)
     out = (C,)
     if return_sums:
         out += (S,)
@@ -141,10 +144,10 @@ def gemm_nn(A, B, dtype: int, rows=None, return_sums=False, return_count=False):
     return out[0] if len(out) == 1 else out
 
 
-def gemm_points(A, B, layout: str, dtype: int, rows, cols, return_sums=False):
+def gemm_points(A, B, layout: str, dtype: int, rows, cols, return_sums=False, relu=False):
     """Elements C[rows[i], cols[i]], each as an ascending-k binary32 dot product.
 
-    layout is "nt" (B [N,K]) or "nn" (B [K,N]).
+    layout is "nt" (B [N,K]) or "nn" (B [K,N]); relu as for gemm_nt.
     """
     A = _u16(A)
     B = _u16(B)
@@ -164,7 +167,8 @@ def gemm_points(A, B, layout: str, dtype: int, rows, cols, return_sums=False):
     C = np.empty(rows.shape, dtype=np.uint16)
     S = np.empty(rows.shape, dtype=np.float32)
     rc = _load().oracle_gemm_points(_ptr(A, ctypes.c_uint16), _ptr(B, ctypes.c_uint16), b_layout,
-                                    M, N, K, dtype, _ptr(rows, ctypes.c_int64), _ptr(cols, ctypes.c_int64),
+                                    M, N, K, dtype, int(bool(relu)), _ptr(rows, ctypes.c_int64),
+                                    _ptr(cols, ctypes.c_int64),
                                     rows.size, _ptr(C, ctypes.c_uint16), _ptr(S, ctypes.c_float))
     if rc != 0:
         raise ValueError("oracle_gemm_points rejected its arguments")

@@ -16,6 +16,9 @@
  * ties to even), and round() narrows the binary32 sum back to the input format
  * with round-to-nearest-even.
  *
+ * With the ReLU epilogue the binary32 sum s becomes relu(s) = (s > 0 ? s : +0)
+ * before the narrowing (so a NaN sum and -0 both give +0).
+ *
  * Sources:
  *  - TileLang tutorial, chapter 11 "pipeline and autotuning", section 1.1
  *    (the tile loop: clear the fp32 fragment, accumulate A-tile x B-tile^T over
@@ -27,6 +30,11 @@
  *    fp32 accumulation.
  *  - Tilelang-Learning notes "Stage 04 - GEMM", "concepts": the NN form
  *    C[M,N] = A[M,K] @ B[K,N] with fp32 accumulation for fp16/bf16 inputs.
+ *  - TileLang tutorial, chapter 11, section 4.6: the GEMM+ReLU example, a
+ *    pipelined K loop whose result goes through ReLU (max with zero); where
+ *    ReLU sits relative to the narrowing is not stated, and applying it to the
+ *    fp32 sum is the plainest reading (narrowing is monotone and maps 0 to 0,
+ *    so for finite sums either order gives the same encoding).
  *  The accumulation order and the rounding mode are not stated by the pages;
  *  ascending k and round-to-nearest-even are the plainest readings.
  *
@@ -138,10 +146,14 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* The ReLU epilogue on a binary32 sum: s if s > 0, else +0 (NaN included). */
+static float relu_f32(float s) { return s > 0.0f ? s : 0.0f; }
+
 /*
  * Rows [m_begin, m_end) of C.  b_layout selects B stored [N,K] (NT) or [K,N]
- * (NN).  C receives (m_end - m_begin) x N encodings; S, if not NULL, receives
- * the binary32 sums before the final rounding.  fma_count, if not NULL,
+ * (NN); relu = 1 applies the ReLU epilogue.  C receives (m_end - m_begin) x N
+ * encodings; S, if not NULL, receives the binary32 sums before the epilogue
+ * and the final rounding.  fma_count, if not NULL,
  * receives the number of multiply-adds the loops executed.
  *
  * Loop order m, k, n: every C[m,n] still gets its products added one k at a
@@ -152,12 +164,12 @@ int oracle_num_threads(void)
  */
 int oracle_gemm_rows(const uint16_t *A, const uint16_t *B, int b_layout,
                      int64_t M, int64_t N, int64_t K, int dtype,
-                     int64_t m_begin, int64_t m_end,
+                     int64_t m_begin, int64_t m_end, int relu,
                      uint16_t *C, float *S, int64_t *fma_count)
 {
     if (!A || !B || !C || M < 0 || N < 0 || K < 0 || m_begin < 0 ||
         m_end > M || m_begin > m_end || (dtype != ORACLE_F16 && dtype != ORACLE_BF16) ||
-        (b_layout != ORACLE_B_NK && b_layout != ORACLE_B_KN))
+        (b_layout != ORACLE_B_NK && b_layout != ORACLE_B_KN) || (relu != 0 && relu != 1))
         return -1;
     /* Decode B once into a [K,N] binary32 array (a transposed copy for NT). */
     float *Bkn = (float *)malloc((size_t)(K * N > 0 ? K * N : 1) * sizeof(float));
@@ -187,7 +199,7 @@ int oracle_gemm_rows(const uint16_t *A, const uint16_t *B, int b_layout,
         }
         const int64_t r = m - m_begin;
         for (int64_t n = 0; n < N; ++n) {
-            C[r * N + n] = oracle_encode_rne(acc[n], dtype);
+            C[r * N + n] = oracle_encode_rne(relu ? relu_f32(acc[n]) : acc[n], dtype);
             if (S)
                 S[r * N + n] = acc[n];
         }
@@ -205,12 +217,12 @@ int oracle_gemm_rows(const uint16_t *A, const uint16_t *B, int b_layout,
  * shapes too large to compute whole.
  */
 int oracle_gemm_points(const uint16_t *A, const uint16_t *B, int b_layout,
-                       int64_t M, int64_t N, int64_t K, int dtype,
+                       int64_t M, int64_t N, int64_t K, int dtype, int relu,
                        const int64_t *rows, const int64_t *cols, int64_t count,
                        uint16_t *C, float *S)
 {
     if (!A || !B || !C || !rows || !cols || (dtype != ORACLE_F16 && dtype != ORACLE_BF16) ||
-        (b_layout != ORACLE_B_NK && b_layout != ORACLE_B_KN))
+        (b_layout != ORACLE_B_NK && b_layout != ORACLE_B_KN) || (relu != 0 && relu != 1))
         return -1;
     for (int64_t i = 0; i < count; ++i)
         if (rows[i] < 0 || rows[i] >= M || cols[i] < 0 || cols[i] >= N)
@@ -224,7 +236,7 @@ int oracle_gemm_points(const uint16_t *A, const uint16_t *B, int b_layout,
             const float b = oracle_decode(b_layout == ORACLE_B_NK ? B[n * K + k] : B[k * N + n], dtype);
             s = s + a * b;
         }
-        C[i] = oracle_encode_rne(s, dtype);
+        C[i] = oracle_encode_rne(relu ? relu_f32(s) : s, dtype);
         if (S)
             S[i] = s;
     }

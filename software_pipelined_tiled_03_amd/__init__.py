@@ -7,10 +7,12 @@ library; the first call does, and raises if it has not been built.
 """
 from .binding import (GEMM_BF16, GEMM_F16, GEMM_NN, GEMM_NT, AlignmentError, GemmArgumentError, GemmError,
                       GemmHipError, LdsBudgetError, UnsupportedConfigError, gemm_check, gemm_lds_budget,
-                      gemm_lds_bytes, gemm_nn, gemm_nn_raw, gemm_nt, gemm_nt_raw, last_error, load)
+                      gemm_lds_bytes, gemm_nn, gemm_nn_raw, gemm_nn_relu_raw, gemm_nt, gemm_nt_raw, gemm_nt_relu_raw,
+                      last_error, load)
 from .tuning import TuneResult, TuningSpaceError, built_configs, default_config, matmul, plan, prune, tune
 
 __all__ = ["GEMM_BF16", "GEMM_F16", "GEMM_NN", "GEMM_NT", "AlignmentError", "GemmArgumentError", "GemmError",
            "GemmHipError", "LdsBudgetError", "UnsupportedConfigError", "gemm_check", "gemm_lds_budget",
-           "gemm_lds_bytes", "gemm_nn", "gemm_nn_raw", "gemm_nt", "gemm_nt_raw", "last_error", "load",
+           "gemm_lds_bytes", "gemm_nn", "gemm_nn_raw", "gemm_nn_relu_raw", "gemm_nt", "gemm_nt_raw",
+           "gemm_nt_relu_raw", "last_error", "load",
            "TuneResult", "TuningSpaceError", "built_configs", "default_config", "matmul", "plan", "prune", "tune"]

@@ -72,7 +72,7 @@ def load():
                            "(run `python software_pipelined_tiled_03_amd/build.py`)" % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
     i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
-    for name in ("gemm_nt", "gemm_nn"):
+    for name in ("gemm_nt", "gemm_nn", "gemm_nt_relu", "gemm_nn_relu"):
         f = getattr(lib, name)
         f.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, i32, vp]
         f.restype = i32
@@ -111,6 +111,18 @@ def gemm_nn_raw(A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, 
                           hip_stream)
 
 
+def gemm_nt_relu_raw(A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, a_lead, threads, hip_stream):
+    """gemm_nt_relu on raw device addresses; returns the status code."""
+    return load().gemm_nt_relu(A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, a_lead, threads,
+                               hip_stream)
+
+
+def gemm_nn_relu_raw(A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, a_lead, threads, hip_stream):
+    """gemm_nn_relu on raw device addresses; returns the status code."""
+    return load().gemm_nn_relu(A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, a_lead, threads,
+                               hip_stream)
+
+
 def gemm_lds_bytes(block_M, block_N, block_K, num_stages, dtype=GEMM_F16, a_lead=0) -> int:
     return int(load().gemm_lds_bytes(block_M, block_N, block_K, num_stages, a_lead, dtype))
 
@@ -139,7 +151,7 @@ def _dtype_code(t):
     raise GemmArgumentError(GEMM_ERR_ARG, "dtype must be float16 or bfloat16, got %s" % t.dtype)
 
 
-def _gemm(layout, A, B, out, block, num_stages, threads, stream, a_lead):
+def _gemm(layout, A, B, out, block, num_stages, threads, stream, a_lead, relu=False):
     import torch
     if A.dim() != 2 or B.dim() != 2:
         raise GemmArgumentError(GEMM_ERR_ARG, "A and B must be 2-D")
@@ -163,7 +175,11 @@ def _gemm(layout, A, B, out, block, num_stages, threads, stream, a_lead):
     if stream is None:
         stream = torch.cuda.current_stream(A.device).cuda_stream
     bm, bn, bk = block
-    fn = load().gemm_nt if layout == GEMM_NT else load().gemm_nn
+    lib = load()
+    if relu:
+        fn = lib.gemm_nt_relu if layout == GEMM_NT else lib.gemm_nn_relu
+    else:
+        fn = lib.gemm_nt if layout == GEMM_NT else lib.gemm_nn
     with torch.cuda.device(A.device):
         st = fn(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K, _dtype_code(A), bm, bn, bk, num_stages,
                 int(a_lead), threads, stream)
@@ -171,11 +187,13 @@ def _gemm(layout, A, B, out, block, num_stages, threads, stream, a_lead):
     return out
 
 
-def gemm_nt(A, B, out=None, block=(128, 128, 32), num_stages=3, threads=256, stream=None, a_lead=0):
-    """C = A[M,K] @ B[N,K]^T on the GPU (fp16/bf16 in, fp32 accumulate, C in A's dtype)."""
-    return _gemm(GEMM_NT, A, B, out, block, num_stages, threads, stream, a_lead)
+def gemm_nt(A, B, out=None, block=(128, 128, 32), num_stages=3, threads=256, stream=None, a_lead=0, relu=False):
+    """C = A[M,K] @ B[N,K]^T on the GPU (fp16/bf16 in, fp32 accumulate, C in A's dtype);
+    relu=True fuses ReLU into the store (gemm_nt_relu)."""
+    return _gemm(GEMM_NT, A, B, out, block, num_stages, threads, stream, a_lead, relu)
 
 
-def gemm_nn(A, B, out=None, block=(128, 128, 32), num_stages=3, threads=256, stream=None, a_lead=0):
-    """C = A[M,K] @ B[K,N] on the GPU (fp16/bf16 in, fp32 accumulate, C in A's dtype)."""
-    return _gemm(GEMM_NN, A, B, out, block, num_stages, threads, stream, a_lead)
+def gemm_nn(A, B, out=None, block=(128, 128, 32), num_stages=3, threads=256, stream=None, a_lead=0, relu=False):
+    """C = A[M,K] @ B[K,N] on the GPU (fp16/bf16 in, fp32 accumulate, C in A's dtype);
+    relu=True fuses ReLU into the store (gemm_nn_relu)."""
+    return _gemm(GEMM_NN, A, B, out, block, num_stages, threads, stream, a_lead, relu)

@@ -188,7 +188,7 @@ int device_budget(int64_t *out)
 }
 
 int run(int layout, const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype, int bm,
-        int bn, int bk, int stages, int lead, int threads, void *stream)
+        int bn, int bk, int stages, int lead, int threads, void *stream, int relu = 0)
 {
     const void *ptrs[3] = {A, B, C};
     // Argument errors are reported as such even when no device can be queried:
@@ -221,6 +221,7 @@ int run(int layout, const void *A, const void *B, void *C, int64_t M, int64_t N,
     a.tiles_n = (int)((N + bn - 1) / bn);
     a.group_m = a.tiles_m < 4 ? a.tiles_m : 4;
     a.c_vec = (N % 8) == 0 && ((uintptr_t)C & 15) == 0;
+    a.relu = relu;
     const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
     if (grid >= (1LL << 31))
         return fail(GEMM_ERR_UNSUPPORTED, "too many tiles");
@@ -410,6 +411,20 @@ int gemm_nn(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t
 {
     return pipegemm::run(GEMM_NN, A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, a_lead, threads,
                          hip_stream);
+}
+
+int gemm_nt_relu(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype, int block_M,
+                 int block_N, int block_K, int num_stages, int a_lead, int threads, void *hip_stream)
+{
+    return pipegemm::run(GEMM_NT, A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, a_lead, threads,
+                         hip_stream, 1);
+}
+
+int gemm_nn_relu(const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype, int block_M,
+                 int block_N, int block_K, int num_stages, int a_lead, int threads, void *hip_stream)
+{
+    return pipegemm::run(GEMM_NN, A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, a_lead, threads,
+                         hip_stream, 1);
 }
 
 int64_t gemm_lds_bytes(int block_M, int block_N, int block_K, int num_stages, int a_lead, int dtype)

@@ -71,6 +71,7 @@ struct KernelArgs {
     int tiles_n;  // ceil(N / BN)
     int group_m;  // tile rows swept before advancing along N (L2 reuse)
     int c_vec;    // 1 when C rows allow 16-byte stores (N % 8 == 0, C 16-byte aligned)
+    int relu;     // 1: C = relu(A.B), the fp32 sum s replaced by (s > 0 ? s : +0) before rounding
 };
 
 // ---------------------------------------------------------------------------
@@ -599,8 +600,12 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
                 for (int q = 0; q < 4; ++q) {
                     typename E::quad v;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        v[r] = (T)acc[f][gp * G + gb][4 * q + r];
+                    for (int r = 0; r < 4; ++r) {
+                        float x = acc[f][gp * G + gb][4 * q + r];
+                        if (p.relu)
+                            x = x > 0.f ? x : 0.f;
+                        v[r] = (T)x;
+                    }
                     *(typename E::quad *)(strip + cbuf_half_offset(lr, 4 * gb + q, lh, G)) = v;
                 }
             // strip -> C: lane takes 16 bytes (8 columns) of one row

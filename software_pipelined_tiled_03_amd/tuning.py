@@ -186,8 +186,9 @@ def tune(A, B, layout="nt", configs=None, warmup=25, reps=100, out=None, stream=
 _tuned = {}
 
 
-def matmul(A, B, layout="nt", autotune=False, out=None, stream=None):
-    """C = A @ B^T (layout 'nt', B [N,K]) or A @ B ('nn', B [K,N]).
+def matmul(A, B, layout="nt", autotune=False, out=None, stream=None, relu=False):
+    """C = A @ B^T (layout 'nt', B [N,K]) or A @ B ('nn', B [K,N]); relu=True
+    fuses ReLU into the store.
 
     autotune=False uses default_config (the fixed gfx950 table).  autotune=True
     tunes once per (layout, M, N, K, dtype) in this process and then reuses the
@@ -206,4 +207,4 @@ def matmul(A, B, layout="nt", autotune=False, out=None, stream=None):
         cfg = default_config(lc, M, N, K, dtype)
     fn = _b.gemm_nt if lc == _b.GEMM_NT else _b.gemm_nn
     return fn(A, B, out=out, block=(cfg["block_M"], cfg["block_N"], cfg["block_K"]), num_stages=cfg["num_stages"],
-              threads=cfg["threads"], stream=stream, a_lead=cfg["a_lead"])
+              threads=cfg["threads"], stream=stream, a_lead=cfg["a_lead"], relu=relu)

@@ -286,3 +286,61 @@ def test_alignment_and_argument_errors():
     with pytest.raises(pg.GemmArgumentError):
         pg.gemm_nt(dA, dB, threads=100)
     assert pg.gemm_lds_budget() == 160 * 1024
+
+
+# --------------------------------------------------------------------------
+# The fused ReLU epilogue (gemm_nt_relu / gemm_nn_relu)
+
+def run_relu(layout, A, B, dtype, M, N, K, block, stages, threads, a_lead=0):
+    dA, dB = dev(A, dtype), dev(B, dtype)
+    fn = pg.gemm_nt if layout == "nt" else pg.gemm_nn
+    C = fn(dA.view(M, K), dB.view(B.shape), block=block, num_stages=stages, threads=threads, a_lead=a_lead,
+           relu=True)
+    torch.cuda.synchronize()
+    return host(C)
+
+
+def relu_of(bits, dtype, og):
+    return np.where(og.decode(bits, dtype) > 0, bits, np.uint16(0))
+
+
+@pytest.mark.parametrize("tile", [(128, 128, 32, 256), (256, 256, 64, 256), (128, 256, 64, 256)],
+                         ids=lambda t: "%dx%dx%d_t%d" % t)
+@pytest.mark.parametrize("layout,dtype", [("nt", F16), ("nn", BF16)])
+def test_relu_ragged(oracle_gemm, tile, layout, dtype):
+    bm, bn, bk, th = tile
+    M, N, K = 2 * bm + 37, 2 * bn + 24, 5 * bk + 8
+    wl = inputs.custom(layout, dtype, M, N, K, seed=311 + bm + bn + bk + dtype)
+    A, B = wl.make()
+    fn = oracle_gemm.gemm_nt if layout == "nt" else oracle_gemm.gemm_nn
+    want = fn(A, B, dtype, relu=True)
+    plain = run(layout, A, B, dtype, M, N, K, (bm, bn, bk), 2, th)
+    got = run_relu(layout, A, B, dtype, M, N, K, (bm, bn, bk), 2, th)
+    assert_close(got, want, dtype, oracle_gemm, "relu %s %s" % (layout, tile))
+    # the fused epilogue is exactly ReLU of the kernel's own result
+    assert np.array_equal(got, relu_of(plain, dtype, oracle_gemm))
+    assert (got == 0).any() and (got != 0).any()
+
+
+def test_relu_headline_configuration(oracle_gemm):
+    w = inputs.workload("nt_f16_4096")
+    A, B = w.make()
+    rows = sample_rows(w.M, 256, 21, extra=4)
+    want = np.concatenate([oracle_gemm.gemm_nt(A, B, F16, rows=(r, r + 1), relu=True) for r in rows])
+    got = run_relu("nt", A, B, F16, w.M, w.N, w.K, (256, 256, 64), 2, 256, a_lead=1)
+    assert_close(got[rows], want, F16, oracle_gemm, "relu 4096^3 256x256x64 S=2+A")
+    plain = run("nt", A, B, F16, w.M, w.N, w.K, (256, 256, 64), 2, 256, a_lead=1)
+    assert np.array_equal(got, relu_of(plain, F16, oracle_gemm))
+
+
+def test_relu_nan_sum_gives_positive_zero(oracle_gemm):
+    M, N, K = 64, 128, 64
+    A = inputs.random_matrix((M, K), 22, F16)
+    B = inputs.random_matrix((N, K), 23, F16)
+    A[5, 7] = 0x7E00   # quiet NaN: row 5 of C is NaN, and +0 after the epilogue
+    plain = run("nt", A, B, F16, M, N, K, (128, 128, 32), 2, 256)
+    got = run_relu("nt", A, B, F16, M, N, K, (128, 128, 32), 2, 256)
+    assert np.isnan(oracle_gemm.decode(plain[5], F16)).all()
+    assert (got[5] == 0).all()
+    assert_close(np.delete(got, 5, axis=0), np.delete(oracle_gemm.gemm_nt(A, B, F16, relu=True), 5, axis=0), F16,
+                 oracle_gemm, "relu rows without NaN")

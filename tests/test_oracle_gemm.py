@@ -174,3 +174,58 @@ def test_empty_k_gives_zero(oracle_gemm):
 def test_rejects_mismatched_shapes(oracle_gemm):
     with pytest.raises(ValueError):
         oracle_gemm.gemm_nt(np.zeros((2, 3), np.uint16), np.zeros((2, 4), np.uint16), F16)
+
+
+# --------------------------------------------------------------------------
+# The ReLU epilogue (TileLang tutorial, chapter 11, section 4.6: GEMM+ReLU)
+
+@pytest.mark.parametrize("layout", ["nt", "nn"])
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_relu_of_identity_b_is_elementwise_max_with_zero(oracle_gemm, layout, dtype):
+    # with B = I every sum is one input value, so the epilogue is numpy's
+    # elementwise maximum with zero of A (negative values and zeros become +0)
+    K = 48
+    rng = np.random.default_rng(17)
+    a = rng.uniform(-1, 1, size=(13, K)).astype(np.float32)
+    a[0, :5] = [0.0, -0.0, -1.0, 1.0, -2.0 ** -20]
+    A = _enc(a, dtype)
+    I = _enc(np.eye(K), dtype)
+    fn = oracle_gemm.gemm_nt if layout == "nt" else oracle_gemm.gemm_nn
+    want = _enc(np.maximum(oracle_gemm.decode(A, dtype), np.float32(0)) + np.float32(0), dtype)
+    got = fn(A, I, dtype, relu=True)
+    assert np.array_equal(got, want)
+    assert not (got == (0x8000 if dtype == F16 else 0x8000)).any(), "a negative zero survived the epilogue"
+
+
+@pytest.mark.parametrize("dtype", [F16, BF16])
+def test_relu_commutes_with_the_final_rounding(oracle_gemm, dtype):
+    # rounding to nearest is monotone and maps 0 to 0, so for finite sums
+    # relu-then-round equals round-then-relu (with -0 mapped to +0)
+    rng = np.random.default_rng(18)
+    A = _enc(rng.uniform(-1, 1, size=(37, 70)), dtype)
+    B = _enc(rng.uniform(-1, 1, size=(29, 70)), dtype)
+    plain, sums = oracle_gemm.gemm_nt(A, B, dtype, return_sums=True)
+    fused = oracle_gemm.gemm_nt(A, B, dtype, relu=True)
+    assert np.isfinite(sums).all() and (sums < 0).any() and (sums > 0).any()
+    want = np.where(oracle_gemm.decode(plain, dtype) > 0, plain, np.uint16(0))
+    assert np.array_equal(fused, want)
+
+
+def test_relu_of_a_nan_sum_is_positive_zero(oracle_gemm):
+    A = _enc(np.ones((2, 8)), F16)
+    A[1, 3] = 0x7E00  # a quiet NaN in row 1
+    B = _enc(np.ones((3, 8)), F16)
+    plain = oracle_gemm.gemm_nt(A, B, F16)
+    assert (plain[0] == _enc([8.0], F16)[0]).all() and np.isnan(oracle_gemm.decode(plain[1], F16)).all()
+    fused = oracle_gemm.gemm_nt(A, B, F16, relu=True)
+    assert (fused[0] == plain[0]).all() and (fused[1] == 0).all()
+
+
+def test_relu_points_agree_with_rows(oracle_gemm):
+    rng = np.random.default_rng(19)
+    A = _enc(rng.uniform(-1, 1, size=(20, 40)), BF16)
+    B = _enc(rng.uniform(-1, 1, size=(40, 24)), BF16)
+    whole = oracle_gemm.gemm_nn(A, B, BF16, relu=True)
+    rows = rng.integers(0, 20, 30)
+    cols = rng.integers(0, 24, 30)
+    assert np.array_equal(oracle_gemm.gemm_points(A, B, "nn", BF16, rows, cols, relu=True), whole[rows, cols])
