@@ -11,4 +11,5 @@ Contents:
   timeline  -- the discrete-event copy->compute pipeline model.
   budget    -- the multi-buffered on-chip memory budget and the
                configuration-space pruning it implies.
+  attention -- plain softmax attention (the KV-length loop), float64.
 """

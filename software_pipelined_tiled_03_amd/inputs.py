@@ -97,3 +97,54 @@ def workload(name: str) -> Workload:
 def custom(layout: str, dtype: int, M: int, N: int, K: int, seed: int) -> Workload:
     """An ad-hoc workload (tests of edge shapes): seeds seed and seed + 1."""
     return Workload("custom", layout, dtype, M, N, K, seed, seed + 1)
+
+
+# ---------------------------------------------------------------------------
+# Attention (the KV-length loop): Q [B, H, Sq, D], K and V [B, Hkv, Skv, D],
+# each drawn as standard normal float32 and rounded to the dtype (so scores
+# q.k / sqrt(D) are of order one); seeds seed, seed + 1, seed + 2.
+
+@dataclass(frozen=True)
+class AttentionWorkload:
+    name: str
+    dtype: int
+    batch: int
+    heads: int
+    kv_heads: int
+    seq_q: int
+    seq_kv: int
+    dim: int
+    causal: bool
+    seed: int
+
+    def make(self):
+        """(Q, K, V) as uint16 encodings."""
+        q = random_matrix((self.batch * self.heads * self.seq_q, self.dim), self.seed, self.dtype, "normal")
+        k = random_matrix((self.batch * self.kv_heads * self.seq_kv, self.dim), self.seed + 1, self.dtype, "normal")
+        v = random_matrix((self.batch * self.kv_heads * self.seq_kv, self.dim), self.seed + 2, self.dtype, "normal")
+        return (q.reshape(self.batch, self.heads, self.seq_q, self.dim),
+                k.reshape(self.batch, self.kv_heads, self.seq_kv, self.dim),
+                v.reshape(self.batch, self.kv_heads, self.seq_kv, self.dim))
+
+    @property
+    def flops(self) -> int:
+        pairs = self.seq_q * (self.seq_q + 1) // 2 if self.causal else self.seq_q * self.seq_kv
+        return 4 * self.batch * self.heads * self.dim * pairs
+
+
+ATTENTION_WORKLOADS = {
+    "attn_f16_b4_h32_s4096_d128": AttentionWorkload("attn_f16_b4_h32_s4096_d128", F16, 4, 32, 32, 4096, 4096,
+                                                    128, False, 6000),
+    "attn_f16_b4_h32_s4096_d128_causal": AttentionWorkload("attn_f16_b4_h32_s4096_d128_causal", F16, 4, 32, 32,
+                                                           4096, 4096, 128, True, 6100),
+    "attn_bf16_b2_h32_kv8_s2048_d128_causal": AttentionWorkload("attn_bf16_b2_h32_kv8_s2048_d128_causal", BF16,
+                                                                2, 32, 8, 2048, 2048, 128, True, 6200),
+}
+
+
+def attention_workload(name: str) -> AttentionWorkload:
+    return ATTENTION_WORKLOADS[name]
+
+
+def attention_custom(dtype, batch, heads, kv_heads, seq_q, seq_kv, dim, causal, seed) -> AttentionWorkload:
+    return AttentionWorkload("custom", dtype, batch, heads, kv_heads, seq_q, seq_kv, dim, causal, seed)
