@@ -197,3 +197,73 @@ def gemm_nn(A, B, out=None, block=(128, 128, 32), num_stages=3, threads=256, str
     """C = A[M,K] @ B[K,N] on the GPU (fp16/bf16 in, fp32 accumulate, C in A's dtype);
     relu=True fuses ReLU into the store (gemm_nn_relu)."""
     return _gemm(GEMM_NN, A, B, out, block, num_stages, threads, stream, a_lead, relu)
+
+
+# --- attention (include/pipeattn.h) -------------------------------------------
+
+_attn_declared = False
+
+
+def _attn_lib():
+    global _attn_declared
+    lib = load()
+    if not _attn_declared:
+        i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+        lib.attn_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i32, ctypes.c_float, i32, i32,
+                                 i32, i32, vp]
+        lib.attn_fwd.restype = i32
+        lib.attn_lds_bytes.argtypes = [i32, i32, i32]
+        lib.attn_lds_bytes.restype = i64
+        lib.attn_check.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32, i32, i32, i32, i32, i64]
+        lib.attn_check.restype = i32
+        _attn_declared = True
+    return lib
+
+
+def attn_fwd_raw(Q, K, V, O, batch, heads, kv_heads, seq_q, seq_kv, dim, dtype, is_causal, scale, block_M, block_N,
+                 num_stages, threads, hip_stream):
+    """attn_fwd on raw device addresses; returns the status code."""
+    return _attn_lib().attn_fwd(Q, K, V, O, batch, heads, kv_heads, seq_q, seq_kv, dim, dtype, is_causal, scale,
+                                block_M, block_N, num_stages, threads, hip_stream)
+
+
+def attn_lds_bytes(block_N, dim, num_stages) -> int:
+    return int(_attn_lib().attn_lds_bytes(block_N, dim, num_stages))
+
+
+def attn_check(batch, heads, kv_heads, seq_q, seq_kv, dim, dtype, is_causal, block_M, block_N, num_stages, threads,
+               lds_budget) -> int:
+    """Validation only (status code); lds_budget > 0 touches no device."""
+    return int(_attn_lib().attn_check(batch, heads, kv_heads, seq_q, seq_kv, dim, dtype, is_causal, block_M,
+                                      block_N, num_stages, threads, lds_budget))
+
+
+def attention(Q, K, V, causal=False, scale=0.0, out=None, block_M=128, block_N=64, num_stages=2, threads=0,
+              stream=None):
+    """O = softmax(scale Q K^T [causal]) V on the GPU.  Q [B, H, Sq, D], K and V
+    [B, Hkv, Skv, D] contiguous fp16/bf16 device tensors; O like Q."""
+    import torch
+    if Q.dim() != 4 or K.dim() != 4 or V.dim() != 4:
+        raise GemmArgumentError(GEMM_ERR_ARG, "Q, K and V must be 4-D [batch, heads, seq, dim]")
+    if not (Q.is_cuda and K.is_cuda and V.is_cuda):
+        raise GemmArgumentError(GEMM_ERR_ARG, "Q, K and V must be device tensors")
+    if not (Q.is_contiguous() and K.is_contiguous() and V.is_contiguous()):
+        raise GemmArgumentError(GEMM_ERR_ARG, "Q, K and V must be contiguous")
+    if not (Q.dtype == K.dtype == V.dtype):
+        raise GemmArgumentError(GEMM_ERR_ARG, "Q, K and V dtypes differ")
+    B, H, Sq, D = Q.shape
+    if K.shape != V.shape or K.shape[0] != B or K.shape[3] != D:
+        raise GemmArgumentError(GEMM_ERR_ARG, "K and V must be [batch, kv_heads, seq_kv, dim] matching Q")
+    Hkv, Skv = K.shape[1], K.shape[2]
+    if out is None:
+        out = torch.empty_like(Q)
+    elif out.shape != Q.shape or out.dtype != Q.dtype or not out.is_contiguous() or out.device != Q.device:
+        raise GemmArgumentError(GEMM_ERR_ARG, "out must be a contiguous tensor shaped like Q")
+    if stream is None:
+        stream = torch.cuda.current_stream(Q.device).cuda_stream
+    with torch.cuda.device(Q.device):
+        st = attn_fwd_raw(Q.data_ptr(), K.data_ptr(), V.data_ptr(), out.data_ptr(), B, H, Hkv, Sq, Skv, D,
+                          _dtype_code(Q), int(bool(causal)), float(scale), block_M, block_N, num_stages, threads,
+                          stream)
+    _raise_for(st)
+    return out

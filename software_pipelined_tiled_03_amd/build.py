@@ -13,9 +13,11 @@ CSRC = os.path.join(PKG, "csrc")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libpipegemm.so")
 KERNEL_SRC = os.path.join(CSRC, "pipegemm_kernels.hip")
+ATTN_SRC = os.path.join(CSRC, "attn_kernels.hip")
 HOST_SRC = os.path.join(CSRC, "pipegemm.hip")
-DEPS = [KERNEL_SRC, HOST_SRC, os.path.join(CSRC, "pipegemm_kernel.hpp"), os.path.join(CSRC, "pipegemm_launch.hpp"),
-        os.path.join(ROOT, "include", "pipegemm.h")]
+DEPS = [KERNEL_SRC, ATTN_SRC, HOST_SRC] + [os.path.join(CSRC, f) for f in (
+    "pipegemm_kernel.hpp", "pipegemm_launch.hpp", "pipegemm_layout.hpp", "attn_kernel.hpp", "attn_launch.hpp")] + [
+    os.path.join(ROOT, "include", f) for f in ("pipegemm.h", "pipeattn.h")]
 # one kernel translation unit per (element type, B layout, K bound), compiled in parallel
 VARIANTS = [("%s_%s_k%d" % (n, l, kc), e, nn, kc)
             for n, e in (("f16", "_Float16"), ("bf16", "__bf16")) for l, nn in (("nt", 0), ("nn", 1)) for kc in (0, 1)]
@@ -36,6 +38,9 @@ def _compile_cmds(objdir, extra):
         obj = os.path.join(objdir, "kernels_%s.o" % name)
         cmds.append((obj, [HIPCC, *FLAGS, *extra, "-DPG_ELEM=" + elem, "-DPG_NN=%d" % nn,
                            "-DPG_KCHECK=%d" % kcheck, "-c", KERNEL_SRC, "-o", obj]))
+    for name, elem in (("f16", "_Float16"), ("bf16", "__bf16")):
+        obj = os.path.join(objdir, "attn_%s.o" % name)
+        cmds.append((obj, [HIPCC, *FLAGS, *extra, "-DPG_ELEM=" + elem, "-c", ATTN_SRC, "-o", obj]))
     obj = os.path.join(objdir, "host.o")
     cmds.append((obj, [HIPCC, *FLAGS, *extra, "-c", HOST_SRC, "-o", obj]))
     return cmds

@@ -1,0 +1,34 @@
+// Attention kernel instantiations for one element type (PG_ELEM).
+#include "attn_kernel.hpp"
+#include "attn_launch.hpp"
+
+#include <mutex>
+
+#ifndef PG_ELEM
+#error "PG_ELEM must name the element type"
+#endif
+
+namespace pipegemm {
+
+template <class T, int BN, int WAVES>
+hipError_t attn_launch(const AttnArgs &args, int grid, int lds_bytes, hipStream_t stream)
+{
+    using Cfg = AttnTile<BN, WAVES>;
+    static std::once_flag once;
+    static hipError_t attr_err = hipSuccess;
+    std::call_once(once, [] {
+        attr_err = hipFuncSetAttribute((const void *)&attn_kernel<T, Cfg>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       160 * 1024);
+    });
+    if (attr_err != hipSuccess)
+        return attr_err;
+    hipLaunchKernelGGL((attn_kernel<T, Cfg>), dim3(grid), dim3(Cfg::THREADS), lds_bytes, stream, args);
+    return hipGetLastError();
+}
+
+#define PG_ATTN_INSTANTIATE(BN, W) \
+    template hipError_t attn_launch<PG_ELEM, BN, W>(const AttnArgs &, int, int, hipStream_t);
+PG_ATTN_TILE_LIST(PG_ATTN_INSTANTIATE)
+#undef PG_ATTN_INSTANTIATE
+
+}  // namespace pipegemm

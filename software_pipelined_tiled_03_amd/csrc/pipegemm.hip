@@ -1,6 +1,7 @@
 // Host side of the pipelined tiled GEMM: validation, the table of built
 // kernels, and the C-ABI entry points declared in include/pipegemm.h.
 #include "pipegemm.h"
+#include "pipeattn.h"
 
 #include <hip/hip_runtime.h>
 
@@ -9,6 +10,8 @@
 #include <cstdio>
 #include <mutex>
 
+#include "attn_kernel.hpp"
+#include "attn_launch.hpp"
 #include "pipegemm_kernel.hpp"
 #include "pipegemm_launch.hpp"
 
@@ -263,10 +266,155 @@ int64_t tiles_of(int64_t M, int64_t N, int bm, int bn)
     return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
 }
 
+// ---------------------------------------------------------------------------
+// Attention.
+
+typedef hipError_t (*attn_launch_fn)(const AttnArgs &, int grid, int lds_bytes, hipStream_t);
+
+struct AttnInstance {
+    int dtype, bn, waves;
+    int loads_per_wave;  // 1 KiB copies per wave per K/V tile pair
+    attn_launch_fn launch;
+};
+
+#define PG_ATTN_ROW(DT, T, BN, W) {DT, BN, W, 2 * BN * 128 * 2 / (1024 * W), &attn_launch<T, BN, W>},
+#define PG_ATTN_ROW_F16(BN, W) PG_ATTN_ROW(GEMM_F16, _Float16, BN, W)
+#define PG_ATTN_ROW_BF16(BN, W) PG_ATTN_ROW(GEMM_BF16, __bf16, BN, W)
+const AttnInstance kAttnInstances[] = {PG_ATTN_TILE_LIST(PG_ATTN_ROW_F16) PG_ATTN_TILE_LIST(PG_ATTN_ROW_BF16)};
+
+int64_t attn_lds_of(int bn, int dim, int stages)
+{
+    return (int64_t)(stages < 1 ? 1 : stages) * 2 * bn * (int64_t)dim * 2;
+}
+
+int attn_validate(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Skv, int64_t D, int dtype, int causal,
+                  int bm, int bn, int stages, int threads, int64_t budget, const void *const *ptrs,
+                  const AttnInstance **inst)
+{
+    // (1) arguments
+    if (B < 1 || H < 1 || Hkv < 1 || Sq < 1 || Skv < 1 || D < 1)
+        return fail(GEMM_ERR_ARG, "attention sizes must be >= 1");
+    if (H % Hkv)
+        return fail(GEMM_ERR_ARG, "heads (%lld) must be a multiple of kv_heads (%lld)", (long long)H,
+                    (long long)Hkv);
+    if (dtype != GEMM_F16 && dtype != GEMM_BF16)
+        return fail(GEMM_ERR_ARG, "unknown dtype %d", dtype);
+    if (causal != 0 && causal != 1)
+        return fail(GEMM_ERR_ARG, "is_causal must be 0 or 1");
+    if (causal && Sq != Skv)
+        return fail(GEMM_ERR_ARG, "a causal mask needs seq_q == seq_kv");
+    if (bm <= 0 || bn <= 0 || stages < 0)
+        return fail(GEMM_ERR_ARG, "block sizes must be positive and num_stages >= 0");
+    if (threads < 0 || threads % 64 != 0 || threads > 1024)
+        return fail(GEMM_ERR_ARG, "threads must be 0 or a multiple of 64 up to 1024 (got %d)", threads);
+    if (ptrs && (!ptrs[0] || !ptrs[1] || !ptrs[2] || !ptrs[3]))
+        return fail(GEMM_ERR_ARG, "Q, K, V and O must not be null");
+    if (budget <= 0)
+        return fail(GEMM_ERR_ARG, "LDS budget must be positive");
+    // (2) LDS budget: num_stages x (K tile + V tile)
+    const int64_t need = attn_lds_of(bn, (int)(D > (1 << 20) ? (1 << 20) : D), stages);
+    if (need > budget)
+        return fail(GEMM_ERR_LDS_BUDGET,
+                    "LDS budget exceeded: %d stage(s) x 2 x (%d x %lld) x 2 B = %lld B > %lld B available",
+                    stages < 1 ? 1 : stages, bn, (long long)D, (long long)need, (long long)budget);
+    // (3) alignment: 16-byte copies and stores of rows of D elements
+    if (D % 8 != 0)
+        return fail(GEMM_ERR_ALIGN, "dim must be a multiple of 8 (got %lld)", (long long)D);
+    if (ptrs && ((((uintptr_t)ptrs[0]) | ((uintptr_t)ptrs[1]) | ((uintptr_t)ptrs[2]) | ((uintptr_t)ptrs[3])) & 15))
+        return fail(GEMM_ERR_ALIGN, "Q, K, V and O must be 16-byte aligned");
+    // (4) supported configuration and size limits
+    if (D != 128)
+        return fail(GEMM_ERR_UNSUPPORTED, "attention is built for dim 128 (got %lld)", (long long)D);
+    const int th = threads == 0 ? 2 * bm : threads;
+    if (bm % 32 != 0 || th != 2 * bm)
+        return fail(GEMM_ERR_UNSUPPORTED, "block_M must be 32 per wave with threads = 2 x block_M (got %d, %d)", bm,
+                    th);
+    const AttnInstance *in = nullptr;
+    for (const AttnInstance &a : kAttnInstances)
+        if (a.dtype == dtype && a.bn == bn && a.waves == th / 64)
+            in = &a;
+    if (!in)
+        return fail(GEMM_ERR_UNSUPPORTED, "no attention kernel built for block_M %d, block_N %d", bm, bn);
+    const int s = stages < 1 ? 1 : stages;
+    if (s > kAttnMaxStages || (s - 1) * in->loads_per_wave > 63 || attn_lds_of(bn, 128, s) > 160 * 1024)
+        return fail(GEMM_ERR_UNSUPPORTED, "num_stages %d is not built for block_N %d with %d waves", s, bn,
+                    th / 64);
+    const int64_t lim = (int64_t)1 << 31;
+    if (Sq * D * 2 >= lim || Skv * D * 2 >= lim)
+        return fail(GEMM_ERR_UNSUPPORTED, "one head's sequence must be below 2 GiB");
+    if (B * H * ((Sq + bm - 1) / bm) >= lim || B * H >= lim)
+        return fail(GEMM_ERR_UNSUPPORTED, "too many workgroups");
+    if (inst)
+        *inst = in;
+    return ok();
+}
+
 }  // namespace
 }  // namespace pipegemm
 
 extern "C" {
+
+int attn_fwd(const void *Q, const void *K, const void *V, void *O, int64_t batch, int64_t heads, int64_t kv_heads,
+             int64_t seq_q, int64_t seq_kv, int64_t dim, int dtype, int is_causal, float scale, int block_M,
+             int block_N, int num_stages, int threads, void *hip_stream)
+{
+    using namespace pipegemm;
+    const void *ptrs[4] = {Q, K, V, O};
+    int st = attn_validate(batch, heads, kv_heads, seq_q, seq_kv, dim, dtype, is_causal, block_M, block_N,
+                           num_stages, threads, 1LL << 40, ptrs, nullptr);
+    if (st == GEMM_ERR_ARG)
+        return st;
+    int64_t budget = 0;
+    st = device_budget(&budget);
+    if (st != GEMM_OK)
+        return st;
+    const AttnInstance *in = nullptr;
+    st = attn_validate(batch, heads, kv_heads, seq_q, seq_kv, dim, dtype, is_causal, block_M, block_N, num_stages,
+                       threads, budget, ptrs, &in);
+    if (st != GEMM_OK)
+        return st;
+    AttnArgs a;
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.O = O;
+    a.B = (int)batch;
+    a.H = (int)heads;
+    a.Hkv = (int)kv_heads;
+    a.Sq = (int)seq_q;
+    a.Skv = (int)seq_kv;
+    a.groups = (int)(heads / kv_heads);
+    a.causal = is_causal;
+    const float sc = scale > 0.0f ? scale : 1.0f / sqrtf((float)dim);
+    a.scale_log2 = sc * 1.4426950408889634f;  // log2(e)
+    a.stages = num_stages < 1 ? 1 : num_stages;
+    a.nq = (int)((seq_q + block_M - 1) / block_M);
+    const int grid = (int)(batch * heads * a.nq);
+    hipError_t e = in->launch(a, grid, (int)attn_lds_of(block_N, 128, a.stages), (hipStream_t)hip_stream);
+    if (e != hipSuccess)
+        return fail(GEMM_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int64_t attn_lds_bytes(int block_N, int dim, int num_stages)
+{
+    if (block_N < 0 || dim < 0 || num_stages < 0)
+        return -1;
+    return pipegemm::attn_lds_of(block_N, dim, num_stages);
+}
+
+int attn_check(int64_t batch, int64_t heads, int64_t kv_heads, int64_t seq_q, int64_t seq_kv, int64_t dim, int dtype,
+               int is_causal, int block_M, int block_N, int num_stages, int threads, int64_t lds_budget)
+{
+    int64_t budget = lds_budget;
+    if (budget == 0) {
+        const int st = pipegemm::device_budget(&budget);
+        if (st != GEMM_OK)
+            return st;
+    }
+    return pipegemm::attn_validate(batch, heads, kv_heads, seq_q, seq_kv, dim, dtype, is_causal, block_M, block_N,
+                                   num_stages, threads, budget, nullptr, nullptr);
+}
 
 int gemm_configs(int layout, int dtype, gemm_config *out, int max)
 {

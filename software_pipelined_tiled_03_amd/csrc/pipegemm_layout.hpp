@@ -94,6 +94,47 @@ PG_HD constexpr int nn_tr_offset(int lane, int kk, int ncol0, int h)
 }
 
 // ---------------------------------------------------------------------------
+// Attention tiles (head dimension D = 128).
+//
+// The K tile (BN keys x D, D contiguous) is stored as two K-contiguous halves
+// of 64 columns, each laid out like a BK = 64 GEMM tile (so its operand reads
+// reuse the measured kswz<64> swizzle): half hf holds columns 64 hf .. +63.
+template <int BN>
+PG_HD constexpr int attn_k_offset(int r, int c)  // c: 16-byte chunk 0..15 of row r
+{
+    return (c >> 3) * (BN * 128) + k_tile_offset<64>(r, c & 7);
+}
+template <int BN>
+PG_HD constexpr void attn_k_unit(int u, int &r, int &c)
+{
+    int c8 = 0;
+    k_tile_unit<64>(u % (BN * 8), r, c8);
+    c = (u / (BN * 8)) * 8 + c8;
+}
+
+// The V tile (BN keys x D) is stored like the N-contiguous B tile of the NN
+// form with D columns.  O^T = V^T P^T takes V^T as its first MFMA operand:
+// lane l needs column d = dcol0 + (l mod 32) and, in slot j of k-step ks, the
+// key attn_key_of_slot(l, ks, j) -- the order in which the S^T = K Q^T
+// accumulator leaves P in the lane (so P goes to the second operand with no
+// exchange; any order works as long as both operands use the same one).
+PG_HD constexpr int attn_key_of_slot(int lane, int ks, int j)
+{
+    return 16 * ks + 8 * (j >> 2) + 4 * (lane >> 5) + (j & 3);
+}
+// Byte offset of transposed read r (slots 4r .. 4r+3) of that fragment: lane L
+// of 16-lane group G loads row 16 ks + 8 r + 4 (G / 2) + L / 4, columns
+// 4 (L mod 4) .. +3 of the group's 16 (see nn_tr_offset for the exchange).
+template <int D>
+PG_HD constexpr int v_tr_offset(int lane, int ks, int dcol0, int r)
+{
+    const int G = lane >> 4, L = lane & 15;
+    const int n = dcol0 + 16 * (G & 1) + 4 * (L & 3);
+    const int k = 16 * ks + 8 * r + 4 * (G >> 1) + (L >> 2);
+    return n_tile_offset<D>(k, n >> 3) + (n & 7) * 2;
+}
+
+// ---------------------------------------------------------------------------
 // Epilogue staging buffer: each wave turns G of its 32 x 32 output blocks at a
 // time (one 32-row strip, 32 G columns, 2 bytes each) from the MFMA layout
 // into row-major order, so the global stores write whole row segments.

@@ -118,6 +118,63 @@ void check_n_tile(int bk)
             }
 }
 
+// Attention tiles: the copies' destinations match the reads; the V^T
+// transposed reads deliver to lane l, slot j, the key attn_key_of_slot and
+// column dcol0 + l mod 32; the S^T accumulator holds P in that same key order.
+template <int BN>
+void check_attn()
+{
+    constexpr int D = 128;
+    // K: every copied unit is where the operand reads look for it
+    std::set<int> seen;
+    for (int u = 0; u < BN * 16; ++u) {
+        int r = 0, c = 0;
+        attn_k_unit<BN>(u, r, c);
+        CHECK(r >= 0 && r < BN && c >= 0 && c < 16, "attn K unit %d: (%d,%d) outside the tile", u, r, c);
+        CHECK(attn_k_offset<BN>(r, c) == u * 16, "attn K unit %d: written (%d,%d) read elsewhere", u, r, c);
+        seen.insert(r * 16 + c);
+    }
+    CHECK((int)seen.size() == BN * 16, "attn K: units do not cover the tile");
+    // V^T transposed reads
+    for (int ks = 0; ks < BN / 16; ++ks)
+        for (int dcol0 = 0; dcol0 < D; dcol0 += 32)
+            for (int rr = 0; rr < 2; ++rr) {
+                int lk[64], ln[64], word[64];
+                for (int l = 0; l < 64; ++l) {
+                    const int off = v_tr_offset<D>(l, ks, dcol0, rr);
+                    CHECK(off % 8 == 0 && off >= 0 && off + 8 <= BN * D * 2, "attn V: tr read offset %d", off);
+                    word[l] = off / 4;
+                    lk[l] = off / (D * 2);
+                    ln[l] = (((off % (D * 2)) / 16) ^ nswz(lk[l])) * 8 + (off % 16) / 2;
+                }
+                for (int l = 0; l < 64; ++l) {
+                    const int G = l / 16, i = l % 16;
+                    for (int e = 0; e < 4; ++e) {
+                        const int src = 16 * G + 4 * e + i / 4;
+                        const int k = lk[src], n = ln[src] + i % 4;
+                        CHECK(k == attn_key_of_slot(l, ks, 4 * rr + e) && n == dcol0 + l % 32,
+                              "attn V ks=%d dcol0=%d r=%d lane %d elem %d: got (k=%d,n=%d)", ks, dcol0, rr, l, e, k,
+                              n);
+                    }
+                }
+                for (int g = 0; g < 64; g += 16) {
+                    std::set<int> quarters;
+                    for (int l = g; l < g + 16; ++l)
+                        quarters.insert((word[l] * 4 / 64) % 4);
+                    CHECK(quarters.size() == 4, "attn V ks=%d r=%d lanes %d..: rows share a bank quarter", ks, rr, g);
+                }
+            }
+    // P: S^T accumulator element (kb, v) of lane l holds key 32 kb + 8 (v/4) + 4 (l/32) + v%4;
+    // slot j of P fragment ks takes element v = 8 (ks % 2) + j of block kb = ks / 2
+    for (int l = 0; l < 64; ++l)
+        for (int ks = 0; ks < BN / 16; ++ks)
+            for (int j = 0; j < 8; ++j) {
+                const int kb = ks / 2, v = 8 * (ks % 2) + j;
+                CHECK(32 * kb + 8 * (v / 4) + 4 * (l / 32) + v % 4 == attn_key_of_slot(l, ks, j),
+                      "attn P lane %d ks %d slot %d", l, ks, j);
+            }
+}
+
 // Epilogue staging buffer for strips of G output blocks.
 void check_cbuf(int G)
 {
@@ -281,6 +338,8 @@ int main()
     check_n_tile<256>(32);
     check_n_tile<256>(64);
     check_ring();
+    check_attn<64>();
+    check_attn<128>();
     check_cbuf(1);
     check_cbuf(2);
     check_cbuf(4);

@@ -1,0 +1,72 @@
+"""The attention part of the C-ABI on the CPU: pipeattn.h's functions are
+exported, the LDS rule is the pages' (num_stages versioned K and V tiles),
+and validation runs in the documented order without a device."""
+import ctypes
+import os
+import re
+
+from software_pipelined_tiled_03_amd import binding as pg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+MI355X = 160 * 1024
+F16, BF16 = pg.GEMM_F16, pg.GEMM_BF16
+
+
+def declared():
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "pipeattn.h")).read(), flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_and_exports():
+    assert declared() == ["attn_check", "attn_fwd", "attn_lds_bytes"]
+    lib = ctypes.CDLL(pg.LIB_PATH)
+    for name in declared():
+        assert hasattr(lib, name), name
+
+
+def check(B=4, H=32, Hkv=32, Sq=4096, Skv=4096, D=128, dtype=F16, causal=0, bm=128, bn=64, s=2, th=256,
+          budget=MI355X):
+    return pg.attn_check(B, H, Hkv, Sq, Skv, D, dtype, causal, bm, bn, s, th, budget)
+
+
+def test_lds_rule_is_stages_times_k_and_v_tiles():
+    for bn, d, s in [(64, 128, 1), (64, 128, 2), (128, 128, 2), (128, 64, 3)]:
+        assert pg.attn_lds_bytes(bn, d, s) == s * 2 * bn * d * 2
+    assert pg.attn_lds_bytes(64, 128, 0) == pg.attn_lds_bytes(64, 128, 1)
+    assert pg.attn_lds_bytes(-1, 128, 1) == -1
+
+
+def test_budget_checked_before_everything_but_arguments():
+    assert check(bn=128, s=3) == pg.GEMM_ERR_LDS_BUDGET        # 192 KiB
+    assert "LDS budget" in pg.last_error()
+    assert check(bn=128, s=3, D=120) == pg.GEMM_ERR_LDS_BUDGET  # also misaligned and unbuilt
+    assert check(bn=64, s=6) == pg.GEMM_ERR_LDS_BUDGET          # 192 KiB
+    assert check(bn=64, s=5) == pg.GEMM_ERR_UNSUPPORTED         # exactly 160 KiB: fits, not built
+    assert check(bn=64, s=4) == pg.GEMM_OK                      # 128 KiB
+    assert check(bn=128, s=2) == pg.GEMM_OK                     # 128 KiB
+
+
+def test_argument_errors():
+    assert check(Hkv=5) == pg.GEMM_ERR_ARG
+    assert check(causal=1, Skv=2048) == pg.GEMM_ERR_ARG
+    assert check(Sq=0) == pg.GEMM_ERR_ARG
+    assert check(dtype=7) == pg.GEMM_ERR_ARG
+    assert check(th=100) == pg.GEMM_ERR_ARG
+    assert check(s=-1) == pg.GEMM_ERR_ARG
+
+
+def test_alignment_and_unsupported():
+    assert check(D=60) == pg.GEMM_ERR_ALIGN
+    assert check(D=64) == pg.GEMM_ERR_UNSUPPORTED
+    assert check(bm=128, th=512) == pg.GEMM_ERR_UNSUPPORTED     # threads must be 2 x block_M
+    assert check(bm=256, th=512, bn=128) == pg.GEMM_ERR_UNSUPPORTED   # not built
+    assert check(bm=256, th=512, bn=64) == pg.GEMM_OK
+    assert check(bm=256, th=0, bn=64) == pg.GEMM_OK             # default threads = 2 x block_M
+    assert check(bn=32) == pg.GEMM_ERR_UNSUPPORTED
+    assert check(s=5, bn=64, budget=1 << 20) == pg.GEMM_ERR_UNSUPPORTED   # fits a bigger budget, not built
+
+
+def test_grouped_and_causal_configurations_are_valid():
+    assert check(B=2, H=32, Hkv=8, Sq=2048, Skv=2048, dtype=BF16, causal=1) == pg.GEMM_OK
+    assert check(Sq=1, Skv=1) == pg.GEMM_OK
+    assert check(Sq=300, Skv=777) == pg.GEMM_OK

@@ -1,0 +1,103 @@
+"""GPU parity of the attention forward pass (the KV-length loop on the same
+pipelined LDS ring) against the float64 oracle, element by element:
+|gpu - oracle| <= 1e-2 + 1e-2 |oracle| (the tolerance of the GEMM tests; the
+kernel rounds P to the input dtype before the second product, which the
+tolerance covers).  The result must not depend on the ring depth."""
+import numpy as np
+import pytest
+import torch
+
+import software_pipelined_tiled_03_amd as pg
+from oracle import attention as oatt
+from oracle import gemm as og
+from software_pipelined_tiled_03_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+F16, BF16 = inputs.F16, inputs.BF16
+TORCH_DT = {F16: torch.float16, BF16: torch.bfloat16}
+TILES = [(128, 64, 256), (256, 64, 512), (128, 128, 256)]   # (block_M, block_N, threads)
+
+
+def dev(u16, dtype):
+    return torch.from_numpy(np.ascontiguousarray(u16).view(np.int16)).cuda().view(TORCH_DT[dtype])
+
+
+def host(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def run(w, Q, K, V, tile, stages, scale=0.0):
+    bm, bn, th = tile
+    O = pg.attention(dev(Q, w.dtype), dev(K, w.dtype), dev(V, w.dtype), causal=w.causal, scale=scale, block_M=bm,
+                     block_N=bn, num_stages=stages, threads=th)
+    torch.cuda.synchronize()
+    return host(O)
+
+
+def assert_close(got_bits, want, dtype, what):
+    g = og.decode(got_bits, dtype).astype(np.float64)
+    assert np.isfinite(g).all(), what + ": non-finite output"
+    err = np.abs(g - want)
+    bad = err > 1e-2 + 1e-2 * np.abs(want)
+    assert not bad.any(), "%s: %d of %d outside tolerance, max err %.3g at %s" % (
+        what, int(bad.sum()), bad.size, err.max(), np.argwhere(bad)[:3].tolist())
+
+
+@pytest.mark.parametrize("tile", TILES, ids=lambda t: "bm%d_bn%d_t%d" % t)
+@pytest.mark.parametrize("dtype,causal", [(F16, False), (F16, True), (BF16, True)])
+def test_ragged_every_tile_every_depth(tile, dtype, causal):
+    # 300 queries and keys: ragged against block_M and block_N; 4 query heads on 2 KV heads
+    w = inputs.attention_custom(dtype, 2, 4, 2, 300, 300, 128, causal, seed=700 + dtype + 2 * causal + tile[1])
+    Q, K, V = w.make()
+    want = oatt.attention(Q, K, V, dtype, causal=causal)
+    first = None
+    for s in (1, 2, 3, 4):
+        if pg.attn_check(2, 4, 2, 300, 300, 128, dtype, int(causal), tile[0], tile[1], s, tile[2], 160 * 1024):
+            continue
+        got = run(w, Q, K, V, tile, s)
+        assert_close(got, want, dtype, "tile %s S=%d" % (tile, s))
+        if first is None:
+            first = got
+        else:
+            assert np.array_equal(got, first), "ring depth %d changed the result" % s
+
+
+@pytest.mark.parametrize("Sq,Skv", [(200, 333), (1, 77), (130, 1), (64, 64)])
+def test_unequal_and_tiny_lengths(Sq, Skv):
+    w = inputs.attention_custom(F16, 1, 2, 1, Sq, Skv, 128, False, seed=800 + Sq + Skv)
+    Q, K, V = w.make()
+    want = oatt.attention(Q, K, V, F16)
+    assert_close(run(w, Q, K, V, (128, 64, 256), 2), want, F16, "Sq=%d Skv=%d" % (Sq, Skv))
+
+
+def test_explicit_scale():
+    w = inputs.attention_custom(BF16, 1, 2, 2, 257, 257, 128, True, seed=900)
+    Q, K, V = w.make()
+    want = oatt.attention(Q, K, V, BF16, causal=True, scale=0.3)
+    assert_close(run(w, Q, K, V, (256, 64, 512), 3, scale=0.3), want, BF16, "scale 0.3")
+
+
+@pytest.mark.parametrize("name", ["attn_f16_b4_h32_s4096_d128", "attn_f16_b4_h32_s4096_d128_causal",
+                                  "attn_bf16_b2_h32_kv8_s2048_d128_causal"])
+def test_full_size_sampled_rows(name):
+    w = inputs.attention_workload(name)
+    Q, K, V = w.make()
+    got = run(w, Q, K, V, (128, 64, 256), 2)
+    rng = np.random.default_rng(11)
+    for b, h in [(0, 0), (w.batch - 1, w.heads - 1), (w.batch // 2, 5)]:
+        rows = np.unique(np.concatenate([[0, 1, 127, 128, w.seq_q - 1], rng.integers(0, w.seq_q, 8)]))
+        want = oatt.attention_rows(Q, K, V, w.dtype, b, h, rows, causal=w.causal)
+        assert_close(got[b, h, rows], want, w.dtype, "%s b=%d h=%d" % (name, b, h))
+
+
+def test_errors_leave_output_untouched():
+    q = torch.zeros((1, 3, 64, 128), dtype=torch.float16, device="cuda")
+    k = torch.zeros((1, 2, 64, 128), dtype=torch.float16, device="cuda")
+    out = torch.full_like(q, 5.0)
+    with pytest.raises(pg.GemmArgumentError):
+        pg.attention(q, k, k, out=out)     # 3 heads on 2 KV heads
+    with pytest.raises(pg.LdsBudgetError):
+        pg.attention(q[:, :2], k, k, out=out[:, :2].contiguous(), block_N=128, num_stages=3)
+    torch.cuda.synchronize()
+    assert bool((out == 5.0).all())
