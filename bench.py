@@ -38,6 +38,12 @@ def parse_depth(d):
     """'3' -> (3, 0); '2+A' -> (2, 1)."""
     d = str(d)
     return (int(d[:-2]), 1) if d.endswith("+A") else (int(d), 0)
+# The attention KV-length loop on the same ring: (workload, (block_M, block_N, threads), ring depths)
+ATTENTION = [
+    ("attn_f16_b4_h32_s4096_d128", (256, 64, 512), (1, 2, 3, 4)),
+    ("attn_f16_b4_h32_s4096_d128_causal", (256, 64, 512), (1, 2, 3, 4)),
+    ("attn_f16_b4_h32_s4096_d128", (128, 64, 256), (1, 2, 3, 4)),
+]
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -118,6 +124,47 @@ def time_gemm(fn, dA, dB, C, block, stages, threads, steps, warmup, a_lead=0, re
     return start.elapsed_time(end) / steps
 
 
+def attention_sweep(steps=10, warmup=3):
+    """TFLOP/s (4 B H D x visible query-key pairs / t) of the attention kernel
+    per ring depth on the ATTENTION workloads."""
+    import numpy as np
+    import torch
+
+    import software_pipelined_tiled_03_amd as pg
+    from software_pipelined_tiled_03_amd import inputs
+
+    out = {}
+    tensors = {}
+    for name, (bm, bn, th), depths in ATTENTION:
+        w = inputs.attention_workload(name)
+        if name not in tensors:
+            tdt = torch.float16 if w.dtype == inputs.F16 else torch.bfloat16
+            tensors[name] = [torch.from_numpy(x.view(np.int16)).cuda().view(tdt) for x in w.make()]
+        dQ, dK, dV = tensors[name]
+        O = torch.empty_like(dQ)
+        row = {}
+        for s in depths:
+            def call():
+                pg.attention(dQ, dK, dV, causal=w.causal, out=O, block_M=bm, block_N=bn, num_stages=s, threads=th)
+            for _ in range(warmup):
+                call()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            row[str(s)] = dict(tflops=round(w.flops / ms / 1e9, 1), ms=round(ms, 4),
+                               lds_bytes=pg.attn_lds_bytes(bn, 128, s))
+            _log("attention %s bm%d bn%d S=%d: %.1f TFLOP/s" % (name, bm, bn, s, w.flops / ms / 1e9))
+        out["%s_bm%d_bn%d_t%d" % (name, bm, bn, th)] = row
+    del tensors
+    return out
+
+
 def cpu_baseline(w, A, B, rows):
     """The CPU oracle (as it stands) on the first `rows` rows of C."""
     from oracle import gemm as og
@@ -139,6 +186,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-attention", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-context", action="store_true", help="skip the torch.matmul context timing")
@@ -222,6 +270,8 @@ def main():
     _log("headline %s tile %s S=%d%s threads=%d: %.3f ms, %.1f TFLOP/s"
          % (w.name, block, stages, "+A" if a_lead else "", threads, ms, tflops))
 
+    attn = None if args.no_attention or args.no_sweep else attention_sweep()
+
     # the fused GEMM+ReLU epilogue in the same configuration
     relu_ms = time_gemm(fn, dA, dB, C, block, stages, threads, steps=max(10, args.steps // 2), warmup=args.warmup,
                         a_lead=a_lead, relu=True)
@@ -274,6 +324,7 @@ def main():
         "cpu_baseline": cpu,
         "per_num_stages": sweep,
         "fused_relu": {"tflops": round(flops / relu_ms / 1e9, 2), "ms_per_step": round(relu_ms, 5)},
+        "attention": attn,
         "context_torch_matmul_tflops": ref,
     }
     print(json.dumps(out), flush=True)
