@@ -517,13 +517,11 @@ int gemm_default_config(int layout, int64_t M, int64_t N, int64_t K, int dtype, 
         K < 0 || out == nullptr)
         return pipegemm::fail(GEMM_ERR_ARG, "gemm_default_config: bad arguments");
     // Largest tile first; the first whose grid fills the 256 CUs wins, else the
-    // one with the most workgroups.  The ring of each tile is its fastest
-    // measured one on MI355X (256x256x64: two stages + leading A).  Tuning the
-    // built space on seven shapes from 1024x1024x8192 to 16384x4096x4096 puts
-    // this choice within 1 % of the winner, except that for K <= 1024 the
-    // 256x256x64 tile is faster with 8 waves (5 % at 4096x4096x512).
+    // one with the most workgroups.  The ring and wave count of each tile are
+    // its fastest measured ones on MI355X (256x256x64: 8 waves, two stages +
+    // leading A).
     static const gemm_config kTable[] = {
-        {256, 256, 64, 2, 1, 256},
+        {256, 256, 64, 2, 1, 512},
         {256, 128, 64, 3, 0, 256},
         {128, 256, 64, 3, 1, 256},
         {128, 128, 64, 4, 0, 256},
@@ -542,8 +540,6 @@ int gemm_default_config(int layout, int64_t M, int64_t N, int64_t K, int dtype, 
         }
     }
     *out = *pick;
-    if (out->block_M == 256 && out->block_N == 256 && K <= 1024)
-        out->threads = 512;
     return pipegemm::ok();
 }
 

@@ -28,12 +28,16 @@
 //    by choosing which global 16-byte chunk each lane fetches;
 //  - the copy wait is s_waitcnt vmcnt(n), n = loads still allowed in flight
 //    (the copies of the tiles issued after kt); vmcnt counts in issue order;
-//  - compute: v_mfma_f32_32x32x16_{f16,bf16}, 16 fp32 accumulators per lane
-//    per 32x32 block, operands read from LDS with ds_read_b128 (k-contiguous
-//    tiles) or ds_read_b64_tr_b16 (the N-contiguous B tile of the NN form);
+//  - compute: v_mfma_f32_16x16x32_{f16,bf16} (4 fp32 accumulators per lane
+//    per 16x16 block) or v_mfma_f32_32x32x16_{f16,bf16} (16 per 32x32 block),
+//    operands read from LDS with ds_read_b128 (k-contiguous tiles) or
+//    ds_read_b64_tr_b16 (the N-contiguous B tile of the NN form).  The two
+//    shapes run at the same nominal rate, but with random operands the 16x16
+//    one draws less power per flop (half the accumulator traffic per flop),
+//    so the power-limited clock stays higher;
 //  - the MFMA is fed the B fragment as its first operand and the A fragment as
 //    its second, so it produces C^T blocks: each lane then holds 4 consecutive
-//    columns of one row of C and the epilogue stores 8 bytes at a time;
+//    columns of one row of C;
 //  - out-of-range rows and K/N chunks read as zero through the buffer
 //    resource's range check (an offset at or beyond num_records returns 0).
 #pragma once
@@ -55,6 +59,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -99,17 +104,69 @@ struct Elem<__bf16> {
     }
 };
 
+// The GEMM's MFMA per block shape MF (32: 32x32x16, 16: 16x16x32), fed
+// (B fragment, A fragment, accumulator).
+template <class T, int MF>
+struct Mfma;
+
+template <>
+struct Mfma<_Float16, 32> {
+    typedef f32x16 acc;
+    static __device__ __forceinline__ acc run(f16x8 b, f16x8 a, acc c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c, 0, 0, 0);
+    }
+};
+
+template <>
+struct Mfma<_Float16, 16> {
+    typedef f32x4 acc;
+    static __device__ __forceinline__ acc run(f16x8 b, f16x8 a, acc c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a, c, 0, 0, 0);
+    }
+};
+
+template <>
+struct Mfma<__bf16, 32> {
+    typedef f32x16 acc;
+    static __device__ __forceinline__ acc run(bf16x8 b, bf16x8 a, acc c)
+    {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
+    }
+};
+
+template <>
+struct Mfma<__bf16, 16> {
+    typedef f32x4 acc;
+    static __device__ __forceinline__ acc run(bf16x8 b, bf16x8 a, acc c)
+    {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, a, c, 0, 0, 0);
+    }
+};
+
 // ---------------------------------------------------------------------------
 // Tile geometry.  WM x WN waves; each wave owns a TM x TN sub-tile of C made
-// of FM x FN blocks of 32 x 32.
-template <int BM_, int BN_, int BK_, int WM_, int WN_>
+// of FM x FN blocks of MF x MF (the MFMA shape).
+//
+// The shape follows the waves per SIMD.  With 8 waves (two per SIMD, at most
+// 256 registers each) the accumulators live in VGPRs and the 16x16x32 MFMA
+// runs without overhead, so it is used for its lower power.  With 4 waves
+// (one per SIMD) the accumulators go to AGPRs, where the compiler keeps
+// 16x16x32 accumulators only by copying them inside the K loop (hundreds of
+// v_accvgpr moves per tile); 32x32x16 accumulators stay in place.
+template <int WAVES>
+constexpr int default_mfma() { return WAVES >= 8 ? 16 : 32; }
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int MF_ = default_mfma<WM_ * WN_>()>
 struct Tile {
-    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_, MF = MF_;
     static constexpr int WAVES = WM * WN;
     static constexpr int THREADS = 64 * WAVES;
     static constexpr int TM = BM / WM, TN = BN / WN;
-    static constexpr int FM = TM / 32, FN = TN / 32;
-    static constexpr int KSTEPS = BK / 16;             // MFMA k-steps per tile
+    static constexpr int FM = TM / MF, FN = TN / MF;
+    static constexpr int KPS = 512 / MF;               // k per MFMA: 16 (32x32) or 32 (16x16)
+    static constexpr int KSTEPS = BK / KPS;            // MFMA k-steps per tile
     static constexpr int A_BYTES = BM * BK * 2;
     static constexpr int B_BYTES = BN * BK * 2;
     static constexpr int SLOT_BYTES = A_BYTES + B_BYTES;
@@ -117,7 +174,8 @@ struct Tile {
     static constexpr int B_LOADS = B_BYTES / (1024 * WAVES);
     static constexpr int LOADS = A_LOADS + B_LOADS;
     static_assert(BM % WM == 0 && BN % WN == 0, "waves must split the tile");
-    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave sub-tiles are made of 32x32 blocks");
+    static_assert(MF == 16 || MF == 32, "MFMA blocks are 16x16 or 32x32");
+    static_assert(TM % MF == 0 && TN % MF == 0, "wave sub-tiles are made of MFMA blocks");
     static_assert(BK == 32 || BK == 64, "block_K must be 32 or 64");
     static_assert(A_BYTES % (1024 * WAVES) == 0 && B_BYTES % (1024 * WAVES) == 0,
                   "each wave must copy a whole number of 1 KiB pieces of each tile");
@@ -216,23 +274,27 @@ __device__ __forceinline__ void static_for(F &&f)
 }
 
 // Scheduling hint for one stretch of NM MFMAs: LDS reads (NR) go out as early
-// as possible, two per MFMA, and global loads (NL) are spread evenly after
-// them, so both issue while the matrix core is busy.
-template <int NM, int NR, int NL, int... I>
+// as possible, RPM per MFMA, and global loads (NL) are spread evenly after
+// them, so both issue while the matrix core is busy.  RPM is 2 for the
+// 32-cycle 32x32x16 MFMA and 1 for the 16-cycle 16x16x32 one: one 1 KiB read
+// per 16 cycles per wave is what the LDS command queue sustains with two waves
+// per SIMD (twice that rate fills it and stalls the issuing wave).
+template <int NM, int NR, int NL, int RPM, int... I>
 __device__ __forceinline__ void interleave_impl(std::integer_sequence<int, I...>)
 {
     ((__builtin_amdgcn_sched_group_barrier(0x008, 1, 0),
-      (2 * I < NR ? __builtin_amdgcn_sched_group_barrier(0x100, (NR - 2 * I) < 2 ? (NR - 2 * I) : 2, 0) : (void)0),
+      (RPM * I < NR ? __builtin_amdgcn_sched_group_barrier(0x100, (NR - RPM * I) < RPM ? (NR - RPM * I) : RPM, 0)
+                    : (void)0),
       ((I + 1) * NL / NM - I * NL / NM > 0
            ? __builtin_amdgcn_sched_group_barrier(0x020, (I + 1) * NL / NM - I * NL / NM, 0)
            : (void)0)),
      ...);
 }
 
-template <int NM, int NR, int NL>
+template <int NM, int NR, int NL, int RPM = 2>
 __device__ __forceinline__ void interleave()
 {
-    interleave_impl<NM, NR, NL>(std::make_integer_sequence<int, NM>());
+    interleave_impl<NM, NR, NL, RPM>(std::make_integer_sequence<int, NM>());
 }
 
 // ---------------------------------------------------------------------------
@@ -260,7 +322,9 @@ __device__ __forceinline__ typename Elem<T>::frag load_b_nn(const char *slot, in
     i16x8 out;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const i16x4 v = ds_read_tr16_b64(slot + nn_tr_offset<Cfg::BN>(lane, kk, ncol0, h));
+        const int off = Cfg::MF == 32 ? nn_tr_offset<Cfg::BN>(lane, kk, ncol0, h)
+                                      : nn_tr_offset16<Cfg::BN>(lane, kk, ncol0, h);
+        const i16x4 v = ds_read_tr16_b64(slot + off);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             out[4 * h + e] = v[e];
@@ -290,8 +354,11 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
 {
     using E = Elem<T>;
     using frag = typename E::frag;
-    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK;
+    using MM = Mfma<T, Cfg::MF>;
+    using accv = typename MM::acc;
+    constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, MF = Cfg::MF;
     constexpr int WAVES = Cfg::WAVES, FM = Cfg::FM, FN = Cfg::FN;
+    constexpr int NACC = MF == 32 ? 16 : 4;  // accumulators per lane per block
 
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
@@ -337,7 +404,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
 #pragma unroll
     for (int t = 0; t < Cfg::A_LOADS; ++t) {
         int r, c;
-        k_tile_unit<BK>((t * WAVES + wave) * 64 + lane, r, c);
+        k_tile_unit<BK, MF>((t * WAVES + wave) * 64 + lane, r, c);
         a_off[t] = (uint32_t)(r * K * 2 + c * 16);
         a_kc[t] = c * 8;
     }
@@ -348,7 +415,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
         const int u = (t * WAVES + wave) * 64 + lane;
         if constexpr (!NN) {
             int r, c;
-            k_tile_unit<BK>(u, r, c);
+            k_tile_unit<BK, MF>(u, r, c);
             b_off[t] = (uint32_t)(r * K * 2 + c * 16);
             b_kc[t] = c * 8;
         } else {
@@ -389,26 +456,27 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
         }
     };
 
-    // Per-lane LDS read offsets of the MFMA operands, per k-step.
-    const int lr = lane & 31, lh = lane >> 5;
+    // Per-lane LDS read offsets of the MFMA operands, per k-step: lane l reads
+    // row l mod MF of a block, chunk (KPS / 8) kk + l / MF.
+    const int lr = lane % MF, lh = lane / MF;
     int a_rd[Cfg::KSTEPS], b_rd[Cfg::KSTEPS];
 #pragma unroll
     for (int kk = 0; kk < Cfg::KSTEPS; ++kk) {
-        // kswz is periodic in 32 rows, so the f-th / g-th 32-row block adds f * 32 * BK * 2
-        a_rd[kk] = k_tile_offset<BK>(wm * Cfg::TM + lr, 2 * kk + lh);
+        // kswz is periodic in 16 rows, so the f-th / g-th block adds f * MF * BK * 2
+        a_rd[kk] = k_tile_offset<BK, MF>(wm * Cfg::TM + lr, (Cfg::KPS / 8) * kk + lh);
         if constexpr (!NN)
-            b_rd[kk] = k_tile_offset<BK>(wn * Cfg::TN + lr, 2 * kk + lh);
+            b_rd[kk] = k_tile_offset<BK, MF>(wn * Cfg::TN + lr, (Cfg::KPS / 8) * kk + lh);
         else
             b_rd[kk] = 0;
     }
 
-    f32x16 acc[FM][FN];
+    accv acc[FM][FN];
 #pragma unroll
     for (int f = 0; f < FM; ++f)
 #pragma unroll
         for (int g = 0; g < FN; ++g)
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
+            for (int v = 0; v < NACC; ++v)
                 acc[f][g][v] = 0.0f;
 
     // MFMA operands, double-buffered: k-step kk computes from buffer kk & 1
@@ -417,13 +485,13 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
     auto read_operands = [&](const char *as, const char *bs, int kk, int buf) {
 #pragma unroll
         for (int f = 0; f < FM; ++f)
-            fa[buf][f] = *(const frag *)(as + a_rd[kk] + f * 32 * BK * 2);
+            fa[buf][f] = *(const frag *)(as + a_rd[kk] + f * MF * BK * 2);
 #pragma unroll
         for (int g = 0; g < FN; ++g) {
             if constexpr (!NN)
-                fb[buf][g] = *(const frag *)(bs + b_rd[kk] + g * 32 * BK * 2);
+                fb[buf][g] = *(const frag *)(bs + b_rd[kk] + g * MF * BK * 2);
             else
-                fb[buf][g] = load_b_nn<T, Cfg>(bs, kk, wn * Cfg::TN + g * 32, lane);
+                fb[buf][g] = load_b_nn<T, Cfg>(bs, kk, wn * Cfg::TN + g * MF, lane);
         }
     };
     // NN form: the operands in buffer `buf` have arrived before any MFMA uses
@@ -438,9 +506,10 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
 #pragma unroll
         for (int i = 0; i < FM * FN; ++i)
             if (i >= first && i < last)
-                acc[i / FN][i % FN] = E::mfma(fb[buf][i % FN], fa[buf][i / FN], acc[i / FN][i % FN]);
+                acc[i / FN][i % FN] = MM::run(fb[buf][i % FN], fa[buf][i / FN], acc[i / FN][i % FN]);
     };
     constexpr int kMfma = FM * FN;
+    constexpr int kRpm = MF == 32 ? 2 : 1;  // LDS reads issued per MFMA
     constexpr int kReads = FM + FN * (NN ? 2 : 1);
     constexpr int kLast = Cfg::KSTEPS - 1;
 
@@ -486,7 +555,11 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
             barrier();
             read_operands(ring_a, ring_b, 0, 0);
             int ra = 0, rb = 0;  // A and B slots of tile kt
-            for (int kt = 0; kt < nk; ++kt) {
+            // One K tile.  Its k-step kk computes from operand buffer (kk + P) & 1;
+            // with an odd number of k-steps per tile the parity P alternates
+            // from tile to tile, so the loop below runs tiles in pairs.
+            auto tile = [&](int kt, auto parity_c) __attribute__((always_inline)) {
+                constexpr int P = decltype(parity_c)::value;
                 const int na = ra + 1 == SA ? 0 : ra + 1, nb = rb + 1 == S ? 0 : rb + 1;
                 const char *as = ring_a + ra * Cfg::A_BYTES, *bs = ring_b + rb * Cfg::B_BYTES;
                 // spread copies go to the slots freed at the previous barrier
@@ -494,7 +567,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
                 char *cbs = ring_b + (rb == 0 ? S - 1 : rb - 1) * Cfg::B_BYTES;
                 const int ta = ring_issue_tile_a(kt, S, LEAD), tb = ring_issue_tile_b(kt, S, LEAD);
                 // the copies k-step kk issues (before its wait, in the last one)
-                auto copies = [&](auto kk_c, auto kk_end_c) {
+                auto copies = [&](auto kk_c, auto kk_end_c) __attribute__((always_inline)) {
                     constexpr int k0 = decltype(kk_c)::value, k1 = decltype(kk_end_c)::value;
                     constexpr int a0 = copy_a_before(k0, kS, kLA, kLB, LEAD), a1 = copy_a_before(k1, kS, kLA, kLB, LEAD);
                     constexpr int b0 = copy_b_before(k0, kS, kLA, kLB, LEAD), b1 = copy_b_before(k1, kS, kLA, kLB, LEAD);
@@ -510,40 +583,51 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
                     return std::integral_constant<int, spread ? (a1 - a0) + (b1 - b0) : 0>();
                 };
                 // every k-step but the last
-                static_for<kLast>([&](auto kk_c) {
+                static_for<kLast>([&](auto kk_c) __attribute__((always_inline)) {
                     constexpr int kk = decltype(kk_c)::value;
-                    sync_operands(kk & 1);
-                    read_operands(as, bs, kk + 1, (kk + 1) & 1);
+                    sync_operands((kk + P) & 1);
+                    read_operands(as, bs, kk + 1, (kk + 1 + P) & 1);
                     auto nl = copies(kk_c, std::integral_constant<int, kk + 1>());
-                    mfmas(kk & 1, 0, kMfma);
-                    interleave<kMfma, kReads, decltype(nl)::value>();
+                    mfmas((kk + P) & 1, 0, kMfma);
+                    interleave<kMfma, kReads, decltype(nl)::value, kRpm>();
                     __builtin_amdgcn_sched_barrier(0);
                 });
                 // last k-step: its operands are in registers; once they have
                 // arrived this wave no longer reads tile kt's slots
+                constexpr int last = (kLast + P) & 1, next = (kS + P) & 1;
                 wait_lds();
-                sync_operands(kLast & 1);
+                sync_operands(last);
                 __builtin_amdgcn_sched_barrier(0);
                 auto nl = copies(std::integral_constant<int, kLast>(), std::integral_constant<int, kS>());
-                mfmas(kLast & 1, 0, kMfma / 2);
-                interleave<kMfma / 2, 0, decltype(nl)::value>();
+                mfmas(last, 0, kMfma / 2);
+                interleave<kMfma / 2, 0, decltype(nl)::value, kRpm>();
                 __builtin_amdgcn_sched_barrier(0);
                 // tile kt+1 has landed once only the copies issued after its
                 // last B copy may be in flight; after the barrier every wave is
                 // done with tile kt's slots and sees tile kt+1
                 wait_vmcnt<ring_wait_steady(S, LEAD, kLA, kLB)>();
                 barrier();
-                read_operands(ring_a + na * Cfg::A_BYTES, ring_b + nb * Cfg::B_BYTES, 0, 0);
+                read_operands(ring_a + na * Cfg::A_BYTES, ring_b + nb * Cfg::B_BYTES, 0, next);
                 if constexpr (!spread) {
                     // burst: tile kt+S into the slots tile kt just freed
                     issue_a(tb, (char *)as, 0, kLA);
                     issue_b(tb, (char *)bs, 0, kLB);
                 }
-                mfmas(kLast & 1, kMfma / 2, kMfma);
-                interleave<kMfma - kMfma / 2, kReads, spread ? 0 : kLA + kLB>();
+                mfmas(last, kMfma / 2, kMfma);
+                interleave<kMfma - kMfma / 2, kReads, spread ? 0 : kLA + kLB, kRpm>();
                 __builtin_amdgcn_sched_barrier(0);
                 ra = na;
                 rb = nb;
+            };
+            if constexpr (kS % 2 == 0) {
+                for (int kt = 0; kt < nk; ++kt)
+                    tile(kt, std::integral_constant<int, 0>());
+            } else {
+                for (int kt = 0; kt < nk; kt += 2) {
+                    tile(kt, std::integral_constant<int, 0>());
+                    if (kt + 1 < nk)
+                        tile(kt + 1, std::integral_constant<int, 1>());
+                }
             }
             // no copy may still be writing LDS when the workgroup ends
             wait_vmcnt<0>();
@@ -577,57 +661,92 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
 
     // Epilogue.  The ring is free once every copy has landed and every wave
     // is past its last LDS read; each wave then stages its output through
-    // its own LDS strip (G blocks of 32 x 32 at a time) so that every global
-    // store writes 16 contiguous bytes per lane and whole row segments per
-    // instruction, instead of 8 bytes in each of 32 rows.
-    constexpr int G = cbuf_blocks(FN, Cfg::SLOT_BYTES / WAVES);
-    constexpr int CH = 4 * G;  // 16-byte chunks per strip row
-    static_assert(2048 * G * WAVES <= Cfg::SLOT_BYTES, "strips must fit in one ring slot");
+    // its own LDS strip so that every global store writes 16 contiguous bytes
+    // per lane and whole row segments per instruction, instead of 8 bytes in
+    // each of 16 or 32 rows.
     wait_vmcnt<0>();
     barrier();
-    char *strip = smem + wave * 2048 * G;
     T *C = (T *)p.C;
     const int M = p.M;
     const int mw = m0 + wm * Cfg::TM, nw = n0 + wn * Cfg::TN;
+    // the fp32 sum of element (block f, g; accumulator v), ReLU applied
+    auto out_value = [&](int f, int g, int v) {
+        float x = acc[f][g][v];
+        if (p.relu)
+            x = x > 0.f ? x : 0.f;
+        return (T)x;
+    };
+    // 16 bytes (8 columns from n) of row m of C; columns past N are skipped
+    auto store_row = [&](int m, int n, i16x8 x) {
+        if (m < M) {
+            short *crow = (short *)(C + (size_t)m * N);
+            if (p.c_vec && n + 7 < N) {
+                *(i16x8 *)(crow + n) = x;
+            } else {
 #pragma unroll
-    for (int f = 0; f < FM; ++f) {
+                for (int e = 0; e < 8; ++e)
+                    if (n + e < N)
+                        crow[n + e] = x[e];
+            }
+        }
+    };
+    if constexpr (MF == 16) {
+        // one strip of 16 rows x TN columns per block row f: lane holds row
+        // lr, columns 16 g + 4 lh .. +3 of block g
+        constexpr int TN = Cfg::TN, CH = TN / 8;
+        static_assert(32 * TN * WAVES <= Cfg::SLOT_BYTES, "strips must fit in one ring slot");
+        static_assert((16 * CH) % 64 == 0, "whole strip reads");
+        char *strip = smem + wave * 32 * TN;
 #pragma unroll
-        for (int gp = 0; gp < FN / G; ++gp) {
-            // MFMA layout -> strip: lane holds row lr, columns 32 gb + 8 q + 4 lh .. +3
+        for (int f = 0; f < FM; ++f) {
 #pragma unroll
-            for (int gb = 0; gb < G; ++gb)
+            for (int g = 0; g < FN; ++g) {
+                typename E::quad v;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    typename E::quad v;
+                for (int r = 0; r < 4; ++r)
+                    v[r] = out_value(f, g, r);
+                *(typename E::quad *)(strip + strip_half_offset<TN>(lr, 2 * g + (lh >> 1), lh & 1)) = v;
+            }
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float x = acc[f][gp * G + gb][4 * q + r];
-                        if (p.relu)
-                            x = x > 0.f ? x : 0.f;
-                        v[r] = (T)x;
-                    }
-                    *(typename E::quad *)(strip + cbuf_half_offset(lr, 4 * gb + q, lh, G)) = v;
-                }
-            // strip -> C: lane takes 16 bytes (8 columns) of one row
-#pragma unroll
-            for (int i = 0; i < 2 * G; ++i) {
+            for (int i = 0; i < CH / 4; ++i) {
                 const int idx = i * 64 + lane;
                 const int r = idx / CH, c = idx % CH;
-                i16x8 x = *(const i16x8 *)(strip + cbuf_chunk_offset(r, c, G));
-                if (hswz(r))
+                i16x8 x = *(const i16x8 *)(strip + strip_offset<TN>(r, c));
+                if (r & 1)
                     x = __builtin_shufflevector(x, x, 4, 5, 6, 7, 0, 1, 2, 3);
-                const int m = mw + f * 32 + r;
-                const int n = nw + (gp * G) * 32 + c * 8;
-                if (m < M) {
-                    short *crow = (short *)(C + (size_t)m * N);
-                    if (p.c_vec && n + 7 < N) {
-                        *(i16x8 *)(crow + n) = x;
-                    } else {
+                store_row(mw + f * 16 + r, nw + c * 8, x);
+            }
+        }
+    } else {
+        // G blocks of 32 x 32 at a time (one 32-row strip, 32 G columns)
+        constexpr int G = cbuf_blocks(FN, Cfg::SLOT_BYTES / WAVES);
+        constexpr int CH = 4 * G;  // 16-byte chunks per strip row
+        static_assert(2048 * G * WAVES <= Cfg::SLOT_BYTES, "strips must fit in one ring slot");
+        char *strip = smem + wave * 2048 * G;
 #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            if (n + e < N)
-                                crow[n + e] = x[e];
+        for (int f = 0; f < FM; ++f) {
+#pragma unroll
+            for (int gp = 0; gp < FN / G; ++gp) {
+                // MFMA layout -> strip: lane holds row lr, columns 32 gb + 8 q + 4 lh .. +3
+#pragma unroll
+                for (int gb = 0; gb < G; ++gb)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        typename E::quad v;
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            v[r] = out_value(f, gp * G + gb, 4 * q + r);
+                        *(typename E::quad *)(strip + cbuf_half_offset(lr, 4 * gb + q, lh, G)) = v;
                     }
+                // strip -> C: lane takes 16 bytes (8 columns) of one row
+#pragma unroll
+                for (int i = 0; i < 2 * G; ++i) {
+                    const int idx = i * 64 + lane;
+                    const int r = idx / CH, c = idx % CH;
+                    i16x8 x = *(const i16x8 *)(strip + cbuf_chunk_offset(r, c, G));
+                    if (hswz(r))
+                        x = __builtin_shufflevector(x, x, 4, 5, 6, 7, 0, 1, 2, 3);
+                    store_row(mw + f * 32 + r, nw + (gp * G) * 32 + c * 8, x);
                 }
             }
         }

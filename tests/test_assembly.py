@@ -16,8 +16,8 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "software_pipelined_tiled_03_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-# Tile<128,128,32,2,2>: 4 waves, 2 + 2 one-KiB copies per wave per K tile
-KERNEL = "_ZN8pipegemm11gemm_kernelIDF16_Lb0ENS_4TileILi128ELi128ELi32ELi2ELi2EEELb0EEEvNS_10KernelArgsE"
+# Tile<128,128,32,2,2> (32x32x16 MFMA): 4 waves, 2 + 2 one-KiB copies per wave per K tile
+KERNEL = "_ZN8pipegemm11gemm_kernelIDF16_Lb0ENS_4TileILi128ELi128ELi32ELi2ELi2ELi32EEELb0EEEvNS_10KernelArgsE"
 LA = LB = 2
 
 

@@ -107,7 +107,6 @@ def test_default_config_is_a_built_legal_configuration(shape, layout, dtype):
 
 def test_default_config_of_the_headline_problem():
     assert pg.default_config("nt", 4096, 4096, 4096) == dict(block_M=256, block_N=256, block_K=64, num_stages=2,
-                                                             a_lead=1, threads=256)
-    # short K: 8 waves on the 256x256 tile
+                                                             a_lead=1, threads=512)
     assert pg.default_config("nt", 8192, 8192, 1024)["threads"] == 512
     assert pg.default_config("nt", 2048, 2048, 2048)["block_M"] == 128
