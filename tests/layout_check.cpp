@@ -454,7 +454,7 @@ void check_ring()
     for (int S = 2; S <= 10; ++S)
         for (int lead = 0; lead <= 1; ++lead)
             for (auto &l : loads)
-                for (int ks = 2; ks <= 4; ks += 2)
+                for (int ks : {1, 2, 4})  // k-steps per tile: BK / 16 (32x32x16) or BK / 32 (16x16x32)
                     for (int nk = 0; nk <= 24; ++nk)
                         check_ring_case(S, lead, l[0], l[1], ks, nk);
     for (int n = 1; n <= 32; ++n)
