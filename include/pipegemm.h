@@ -194,13 +194,33 @@ int gemm_prune(int layout, int64_t M, int64_t N, int64_t K, int dtype, const gem
                int64_t lds_budget, int *status);
 
 /*
+ * gemm_rank: an analytic cost for each of the n candidates (chapter 11,
+ * section 3.9: a cost model that knows the hardware orders the search and
+ * flags ties; it does not replace measurement).  cost[i] is a modelled time in
+ * microseconds for an M x N x K problem: per K tile the larger of MFMA time,
+ * copy time (with a measured penalty for block_K = 32) and LDS read time,
+ * plus the copy latency the ring depth leaves uncovered, times the rounds of
+ * workgroups that fit the 256 compute units at the occupancy LDS and an
+ * estimate of the registers allow, plus the C store.  The constants were
+ * fitted to measured gfx950 tuning tables (see the library source); the pages
+ * print no model to pin against, so its only test is how it orders measured
+ * candidates.
+ * Returns GEMM_OK, or GEMM_ERR_ARG for negative sizes, null arrays or a
+ * malformed candidate (threads must be a positive multiple of 128 or 0).
+ * Pure host.
+ */
+int gemm_rank(int64_t M, int64_t N, int64_t K, const gemm_config *cands, int n, double *cost);
+
+/*
  * gemm_tune: measures every candidate whose status[i] is GEMM_OK on the same
  * operands (chapter 11, sections 3.5-3.6): `warmup` launches, then `reps`
  * launches timed together with HIP events on hip_stream.  Writes the mean
  * milliseconds per launch to ms[i] (-1 for skipped candidates) and the index
  * of the fastest to *best (-1 if none ran).  A, B, C and the sizes are as for
- * gemm_nt / gemm_nn (layout selects which); every candidate writes the same C,
- * because the accumulation order over K does not depend on the configuration.
+ * gemm_nt / gemm_nn (layout selects which).  The accumulation order over K
+ * does not depend on the tile or the ring, and the two MFMA shapes gave
+ * bit-identical C on every input tested, so in practice every candidate
+ * writes the same C.
  * Synchronous: returns after the last timed launch has finished.  Returns
  * GEMM_OK or the status of the first failing launch (then the remaining ms[i]
  * are not written).
@@ -214,8 +234,7 @@ int gemm_tune(int layout, const void *A, const void *B, void *C, int64_t M, int6
  * gfx950 without tuning (chapter 11, section 3.8: fix the tuned result as a
  * per-device default): the largest tile whose grid fills the 256 compute
  * units, with the fastest ring measured for that tile, else the tile with the
- * most workgroups (8 waves instead of 4 for the 256 x 256 tile when
- * K <= 1024).  Pure host.  Returns GEMM_OK or GEMM_ERR_ARG.
+ * most workgroups.  Pure host.  Returns GEMM_OK or GEMM_ERR_ARG.
  */
 int gemm_default_config(int layout, int64_t M, int64_t N, int64_t K, int dtype, gemm_config *out);
 

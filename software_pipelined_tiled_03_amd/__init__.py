@@ -10,10 +10,13 @@ from .binding import (GEMM_BF16, GEMM_F16, GEMM_NN, GEMM_NT, AlignmentError, Gem
                       GemmHipError, LdsBudgetError, UnsupportedConfigError, gemm_check, gemm_lds_budget,
                       gemm_lds_bytes, gemm_nn, gemm_nn_raw, gemm_nn_relu_raw, gemm_nt, gemm_nt_raw, gemm_nt_relu_raw,
                       last_error, load)
-from .tuning import TuneResult, TuningSpaceError, built_configs, default_config, matmul, plan, prune, tune
+from .tuning import (RANKED_OUT, TuneResult, TuningSpaceError, built_configs, default_config, matmul, model_costs, plan,
+                     prune, rank, tune)
 
 __all__ = ["GEMM_BF16", "GEMM_F16", "GEMM_NN", "GEMM_NT", "AlignmentError", "GemmArgumentError", "GemmError",
            "GemmHipError", "LdsBudgetError", "UnsupportedConfigError", "gemm_check", "gemm_lds_budget",
            "gemm_lds_bytes", "gemm_nn", "gemm_nn_raw", "gemm_nn_relu_raw", "gemm_nt", "gemm_nt_raw",
            "gemm_nt_relu_raw", "last_error", "load",
-           "attention", "attn_check", "attn_fwd_raw", "attn_lds_bytes", "TuneResult", "TuningSpaceError", "built_configs", "default_config", "matmul", "plan", "prune", "tune"]
+           "attention", "attn_check", "attn_fwd_raw", "attn_lds_bytes",
+           "RANKED_OUT", "TuneResult", "TuningSpaceError", "built_configs", "default_config", "matmul",
+           "model_costs", "plan", "prune", "rank", "tune"]

@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
+
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -266,6 +268,59 @@ int64_t tiles_of(int64_t M, int64_t N, int bm, int bn)
     return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
 }
 
+// Analytic cost of one configuration (microseconds at a nominal 2.1 GHz),
+// used only to order candidates before they are measured (chapter 11, section
+// 3.9: a cost model prunes and ranks, measurement decides).  Per K tile of one
+// workgroup: MFMA time C = 2 bM bN bK / 4096 flop per CU-cycle, divided by
+// 1.2 for the 16x16x32 tiles (their higher clock under the power limit with
+// random operands); copy time X = (bM + bN) bK 2 B at 48 B per cycle, times
+// 1.5 for bK = 32, whose 64-byte rows cost two L2 requests per line; LDS
+// operand reads R = waves (TM + TN) bK 2 B at 128 B per cycle; copy latency
+// L = 2000 cycles.  `occ` workgroups share a compute unit (bounded by LDS and
+// by a register estimate: fp32 accumulators, double-buffered operand
+// fragments and 16 address registers per lane).  With S >= 2 a tile's copies
+// are issued S - 1 tiles ahead (half a tile more with a_lead), so the latency
+// left exposed is max(0, L - (S - 1 + lead / 2) occ max(C, X, R)); with S = 1
+// copy, latency and compute add up.  Each round of occ x 256 workgroups adds
+// the C store (bM bN 2 B per workgroup at 64 B per cycle) and 1000 cycles.
+// The rates and L were fitted to the measured tuning tables of twelve
+// shapes from 512x512x65536 to 16384x4096x4096 (random fp16 operands): the
+// model's first choice is the measured best or within 3 % of it on eleven.
+double model_cost_us(const gemm_config &c, int64_t M, int64_t N, int64_t K)
+{
+    const int W = c.threads / 64 > 0 ? c.threads / 64 : 4;
+    const int MF = W >= 8 ? 16 : 32;
+    const double TM = c.block_M / 2.0, TN = (double)c.block_N / (W / 2);
+    const int S = c.num_stages < 1 ? 1 : c.num_stages;
+    const double lds = (double)lds_bytes_of(c.block_M, c.block_N, c.block_K, S, c.a_lead);
+    const int occ_lds = (int)(163840.0 / lds);
+    const double regs = TM * TN / 64 + 2 * (TM / MF + TN / MF) * 4 + 16;
+    const int waves_simd = (int)(512.0 / regs) < 8 ? (int)(512.0 / regs) : 8;
+    int occ = (4 * waves_simd) / W;
+    if (occ_lds < occ)
+        occ = occ_lds;
+    if (occ < 1)
+        occ = 1;
+    const double tiles = (double)tiles_of(M, N, c.block_M, c.block_N);
+    const double rounds = std::ceil(tiles / (256.0 * occ));
+    const double nk = (double)((K + c.block_K - 1) / c.block_K);
+    const double C = 2.0 * c.block_M * c.block_N * c.block_K / 4096.0 / (MF == 16 ? 1.2 : 1.0);
+    const double X = (c.block_M + c.block_N) * c.block_K * 2.0 / 48.0 * (c.block_K == 32 ? 1.5 : 1.0);
+    const double R = W * (TM + TN) * c.block_K * 2.0 / 128.0;
+    const double L = 2000.0;
+    double tile;
+    if (S == 1) {
+        tile = occ * (C + X) > C + X + L ? occ * (C + X) : C + X + L;
+    } else {
+        double per = C > X ? C : X;
+        per = (per > R ? per : R) * occ;
+        const double hidden = (S - 1 + 0.5 * c.a_lead) * per;
+        tile = per + (L > hidden ? L - hidden : 0.0);
+    }
+    const double epi = occ * c.block_M * c.block_N * 2.0 / 64.0 + 1000.0;
+    return rounds * (nk * tile + epi) / 2100.0;
+}
+
 // ---------------------------------------------------------------------------
 // Attention.
 
@@ -452,6 +507,20 @@ int gemm_prune(int layout, int64_t M, int64_t N, int64_t K, int dtype, const gem
     }
     pipegemm::ok();
     return legal;
+}
+
+int gemm_rank(int64_t M, int64_t N, int64_t K, const gemm_config *cands, int n, double *cost)
+{
+    if (M < 0 || N < 0 || K < 0 || n < 0 || (n > 0 && (cands == nullptr || cost == nullptr)))
+        return pipegemm::fail(GEMM_ERR_ARG, "gemm_rank: bad arguments");
+    for (int i = 0; i < n; ++i) {
+        const gemm_config &c = cands[i];
+        if (c.block_M <= 0 || c.block_N <= 0 || c.block_K <= 0 || c.threads < 0 || c.threads % 128 != 0 ||
+            c.num_stages < 0 || (c.a_lead != 0 && c.a_lead != 1))
+            return pipegemm::fail(GEMM_ERR_ARG, "gemm_rank: candidate %d is malformed", i);
+        cost[i] = pipegemm::model_cost_us(c, M, N, K);
+    }
+    return pipegemm::ok();
 }
 
 int gemm_tune(int layout, const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype,

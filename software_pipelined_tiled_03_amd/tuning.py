@@ -22,7 +22,10 @@ from . import binding as _b
 DEFAULTS = dict(block_M=128, block_N=128, block_K=32, num_stages=3, a_lead=0, threads=256)
 _FIELDS = ("block_M", "block_N", "block_K", "num_stages", "a_lead", "threads")
 GEMM_PRUNE_NODIV = 16
+#: status of a legal candidate that the cost model ranked below the measured top
+RANKED_OUT = 17
 STATUS_TEXT = {_b.GEMM_OK: "ok", GEMM_PRUNE_NODIV: "tile does not divide the problem",
+               RANKED_OUT: "ranked below the measured top by the cost model",
                _b.GEMM_ERR_LDS_BUDGET: "over the LDS budget", _b.GEMM_ERR_UNSUPPORTED: "no kernel built",
                _b.GEMM_ERR_ALIGN: "misaligned", _b.GEMM_ERR_ARG: "bad argument"}
 
@@ -54,6 +57,8 @@ def _lib():
         lib.gemm_tune.restype = i32
         lib.gemm_default_config.argtypes = [i32, i64, i64, i64, i32, pc]
         lib.gemm_default_config.restype = i32
+        lib.gemm_rank.argtypes = [i64, i64, i64, pc, i32, ctypes.POINTER(ctypes.c_double)]
+        lib.gemm_rank.restype = i32
         _declared = True
     return lib
 
@@ -119,6 +124,29 @@ def prune(layout, M, N, K, dtype, configs, lds_budget=0):
     return [int(status[i]) for i in range(n)], legal
 
 
+def model_costs(M, N, K, configs):
+    """The analytic cost (gemm_rank, modelled microseconds) of each config."""
+    n = len(configs)
+    arr = (GemmConfig * max(n, 1))(*[GemmConfig(*[c[f] for f in _FIELDS]) for c in configs])
+    cost = (ctypes.c_double * max(n, 1))()
+    _b._raise_for(_lib().gemm_rank(M, N, K, arr, n, cost))
+    return [float(cost[i]) for i in range(n)]
+
+
+def rank(layout, M, N, K, dtype=_b.GEMM_F16, configs=None, lds_budget=163840):
+    """The legal candidates ordered by the cost model, cheapest first, as
+    (config, modelled microseconds) pairs (chapter 11, section 3.9: the model
+    orders the search; equal costs mean it cannot tell them apart and only
+    measurement can).  Pure host with the default budget (gfx950's 160 KiB);
+    lds_budget 0 takes the current device's."""
+    cands = expand(built_configs(layout, dtype) if configs is None else configs, M, N, K)
+    status, _ = prune(layout, M, N, K, dtype, cands, lds_budget)
+    legal = [c for c, s in zip(cands, status) if s == _b.GEMM_OK]
+    costs = model_costs(M, N, K, legal)
+    order = sorted(range(len(legal)), key=lambda i: (costs[i], i))
+    return [(legal[i], costs[i]) for i in order]
+
+
 def plan(layout, M, N, K, dtype, configs=None, lds_budget=0, allow_single=False):
     """Expand and pre-prune the space, and reject a wasted one before anything
     runs (chapter 11, section 5.3).  Returns (candidates, statuses)."""
@@ -148,9 +176,12 @@ class TuneResult:
                                                                         len(self.table))
 
 
-def tune(A, B, layout="nt", configs=None, warmup=25, reps=100, out=None, stream=None, allow_single=False):
+def tune(A, B, layout="nt", configs=None, warmup=25, reps=100, out=None, stream=None, allow_single=False, top=None):
     """Measure every legal candidate on A, B (device tensors) and return the
-    fastest (gemm_tune).  out receives C (every candidate writes the same C)."""
+    fastest (gemm_tune).  out receives C (every candidate writes the same C).
+
+    top=k measures only the k legal candidates the cost model ranks cheapest
+    (gemm_rank); the others are reported with status RANKED_OUT."""
     import torch
 
     lc = _layout_code(layout)
@@ -164,6 +195,13 @@ def tune(A, B, layout="nt", configs=None, warmup=25, reps=100, out=None, stream=
         raise _b.GemmArgumentError(_b.GEMM_ERR_ARG, "inner dimensions differ")
     dtype = _b._dtype_code(A)
     cands, status = plan(lc, M, N, K, dtype, configs, 0, allow_single)
+    if top is not None:
+        if int(top) < 1:
+            raise ValueError("top must be at least 1")
+        legal = [i for i, s in enumerate(status) if s == _b.GEMM_OK]
+        costs = model_costs(M, N, K, [cands[i] for i in legal])
+        keep = set(legal[j] for j in sorted(range(len(legal)), key=lambda j: (costs[j], j))[:int(top)])
+        status = [s if (s != _b.GEMM_OK or i in keep) else RANKED_OUT for i, s in enumerate(status)]
     if out is None:
         out = torch.empty((M, N), dtype=A.dtype, device=A.device)
     elif out.shape != (M, N) or out.dtype != A.dtype or not out.is_contiguous() or out.device != A.device:

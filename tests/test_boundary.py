@@ -25,7 +25,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["gemm_nt", "gemm_nn", "gemm_nt_relu", "gemm_nn_relu", "gemm_lds_bytes", "gemm_lds_budget", "gemm_check",
-         "gemm_last_error", "gemm_configs", "gemm_prune", "gemm_tune", "gemm_default_config"])
+         "gemm_last_error", "gemm_configs", "gemm_prune", "gemm_rank", "gemm_tune", "gemm_default_config"])
 
 
 def test_library_exports_every_declared_symbol():

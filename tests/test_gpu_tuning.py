@@ -101,3 +101,29 @@ def test_matmul_tunes_once_then_reuses(monkeypatch, oracle_gemm):
     assert len(calls) == 1
     assert np.array_equal(c1, c2) and np.array_equal(c1, c3)
     assert close(c1, oracle_gemm.gemm_nt(A, B, F16), F16, oracle_gemm)
+
+
+def test_tune_top_measures_only_the_models_choice(oracle_gemm):
+    M = N = K = 1024
+    w = inputs.custom("nt", F16, M, N, K, seed=91)
+    A, B = w.make()
+    dA, dB = dev(A, F16).view(M, K), dev(B, F16).view(N, K)
+    res = pg.tune(dA, dB, "nt", warmup=2, reps=5, top=6)
+    measured = [(c, ms) for c, s, ms in res.table if s == 0]
+    ranked_out = [c for c, s, _ in res.table if s == pt.RANKED_OUT]
+    assert len(measured) == 6 and all(ms > 0 for _, ms in measured)
+    top6 = [c for c, _ in pg.rank("nt", M, N, K)[:6]]
+    assert sorted(map(str, (c for c, _ in measured))) == sorted(map(str, top6))
+    assert len(ranked_out) == len(pg.rank("nt", M, N, K)) - 6
+    assert res.config in top6
+
+
+def test_rank_orders_a_measured_table():
+    # a cheap shape: the model's first choice is within 15 % of the measured best
+    M, N, K = 4096, 4096, 512
+    A = (torch.rand(M, K, device="cuda") * 2 - 1).half()
+    B = (torch.rand(N, K, device="cuda") * 2 - 1).half()
+    res = pg.tune(A, B, "nt", warmup=3, reps=10)
+    measured = {str(c): ms for c, s, ms in res.table if s == 0}
+    first = pg.rank("nt", M, N, K)[0][0]
+    assert measured[str(first)] <= 1.15 * res.latency, (first, measured[str(first)], res.config, res.latency)

@@ -110,3 +110,55 @@ def test_default_config_of_the_headline_problem():
                                                              a_lead=1, threads=512)
     assert pg.default_config("nt", 8192, 8192, 1024)["threads"] == 512
     assert pg.default_config("nt", 2048, 2048, 2048)["block_M"] == 128
+
+
+# ---------------------------------------------------------------------------
+# The analytic cost model (gemm_rank; chapter 11, section 3.9: it orders the
+# search, measurement decides).  The pages print no model, so these checks are
+# of its arguments, its ordering contract, and the monotonicity its own
+# definition implies; how well it orders real measurements is a GPU test.
+
+def test_rank_rejects_bad_arguments():
+    bad = dict(pt.DEFAULTS, threads=96)
+    with pytest.raises(pb.GemmArgumentError):
+        pt.model_costs(1024, 1024, 1024, [bad])
+    with pytest.raises(pb.GemmArgumentError):
+        pt.model_costs(-1, 1024, 1024, [dict(pt.DEFAULTS)])
+    with pytest.raises(pb.GemmArgumentError):
+        pt.model_costs(1024, 1024, 1024, [dict(pt.DEFAULTS, a_lead=2)])
+
+
+@pytest.mark.parametrize("shape", [(4096, 4096, 4096), (2048, 2048, 2048), (1024, 1024, 8192), (128, 128, 128)])
+def test_rank_orders_exactly_the_legal_candidates(shape):
+    M, N, K = shape
+    ranked = pg.rank("nt", M, N, K)
+    status, legal = pg.prune("nt", M, N, K, F16, pg.built_configs("nt", F16), MI355X)
+    assert len(ranked) == legal
+    costs = [c for _, c in ranked]
+    assert costs == sorted(costs) and all(c > 0 for c in costs)
+    assert ranked == pg.rank("nt", M, N, K)   # deterministic
+
+
+def test_rank_more_ring_depth_is_never_modelled_slower():
+    # at one workgroup per compute unit (256x256 tiles); where a deeper ring
+    # lowers the occupancy the model may rightly prefer the shallower one
+    for tile, depths in [((256, 256, 32), range(1, 6)), ((256, 256, 64), range(1, 3))]:
+        for threads in (256, 512):
+            cfgs = [dict(block_M=tile[0], block_N=tile[1], block_K=tile[2], num_stages=s, a_lead=0, threads=threads)
+                    for s in depths]
+            costs = pt.model_costs(4096, 4096, 4096, cfgs)
+            assert all(b <= a for a, b in zip(costs, costs[1:])), (tile, threads, costs)
+            assert costs[0] > costs[1]   # S = 1 serialises copy, latency and compute
+
+
+def test_rank_scales_with_the_problem():
+    c = dict(block_M=256, block_N=256, block_K=64, num_stages=2, a_lead=1, threads=512)
+    a, b = pt.model_costs(4096, 4096, 4096, [c])[0], pt.model_costs(4096, 4096, 8192, [c])[0]
+    assert 1.9 < b / a < 2.05          # twice the K tiles, the same fixed store and launch
+    w1, w2 = pt.model_costs(4096, 4096, 4096, [c])[0], pt.model_costs(8192, 4096, 4096, [c])[0]
+    assert 1.95 < w2 / w1 < 2.05       # twice the rounds of workgroups
+
+
+def test_rank_first_choice_at_4096_is_the_measured_fastest():
+    # the measured winner of the 4096^3 fp16 NT tuning table on MI355X
+    assert pg.rank("nt", 4096, 4096, 4096)[0][0] == pg.default_config("nt", 4096, 4096, 4096)
