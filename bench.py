@@ -25,12 +25,16 @@ PEAK_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA, published
 HEADLINE = dict(workload="nt_f16_4096", block=(256, 256, 64), num_stages=2, a_lead=1, threads=512)
 # (label, workload, block, threads, ring depths); a depth "S+A" is num_stages S with a_lead = 1
 SWEEPS = [
+    ("tile128x128x32_t128", "nt_f16_4096", (128, 128, 32), 128, ("1", "2", "3", "4", "6")),
     ("tile128x128x32_t256", "nt_f16_4096", (128, 128, 32), 256, ("1", "2", "3", "4", "6")),
+    ("tile128x128x32_t512", "nt_f16_4096", (128, 128, 32), 512, ("1", "2", "3", "4", "6")),
     ("tile256x256x32_t256", "nt_f16_4096", (256, 256, 32), 256, ("1", "2", "3", "4", "5", "2+A", "3+A")),
     ("tile256x256x32_t512", "nt_f16_4096", (256, 256, 32), 512, ("1", "2", "3", "4", "2+A", "3+A")),
     ("tile256x256x64_t256", "nt_f16_4096", (256, 256, 64), 256, ("1", "2", "2+A")),
     ("tile256x256x64_t512", "nt_f16_4096", (256, 256, 64), 512, ("1", "2", "2+A")),
     ("nn_bf16_tile128x128x32_t256", "nn_bf16_4096", (128, 128, 32), 256, ("3",)),
+    ("nn_bf16_tile128x256x64_t256", "nn_bf16_4096", (128, 256, 64), 256, ("3",)),
+    ("nn_bf16_tile256x128x32_t256", "nn_bf16_4096", (256, 128, 32), 256, ("3",)),
     ("nn_bf16_tile256x256x64_t256", "nn_bf16_4096", (256, 256, 64), 256, ("2", "2+A")),
     ("nn_bf16_tile256x256x64_t512", "nn_bf16_4096", (256, 256, 64), 512, ("2", "2+A")),
 ]
