@@ -585,26 +585,24 @@ int gemm_default_config(int layout, int64_t M, int64_t N, int64_t K, int dtype, 
     if ((layout != GEMM_NT && layout != GEMM_NN) || (dtype != GEMM_F16 && dtype != GEMM_BF16) || M < 0 || N < 0 ||
         K < 0 || out == nullptr)
         return pipegemm::fail(GEMM_ERR_ARG, "gemm_default_config: bad arguments");
-    // Largest tile first; the first whose grid fills the 256 CUs wins, else the
-    // one with the most workgroups.  The ring and wave count of each tile are
-    // its fastest measured ones on MI355X (256x256x64: 8 waves, two stages +
-    // leading A).
+    // One configuration per tile, each with the ring and wave count measured
+    // fastest for it on MI355X (256x256x64: 8 waves, two stages + leading A);
+    // the analytic cost model (gemm_rank) picks among them, so the choice
+    // accounts for how many rounds of workgroups each grid takes on the 256
+    // compute units (a grid just above 256 tiles leaves the second round
+    // nearly empty).  Ties keep the earlier, larger tile.
     static const gemm_config kTable[] = {
         {256, 256, 64, 2, 1, 512},
         {256, 128, 64, 3, 0, 256},
         {128, 256, 64, 3, 1, 256},
         {128, 128, 64, 4, 0, 256},
     };
-    const gemm_config *pick = nullptr;
-    int64_t most = -1;
+    const gemm_config *pick = &kTable[0];
+    double best = pipegemm::model_cost_us(kTable[0], M, N, K);
     for (const gemm_config &c : kTable) {
-        const int64_t t = pipegemm::tiles_of(M, N, c.block_M, c.block_N);
-        if (t >= 256) {
-            pick = &c;
-            break;
-        }
-        if (t > most) {
-            most = t;
+        const double cost = pipegemm::model_cost_us(c, M, N, K);
+        if (cost < best) {
+            best = cost;
             pick = &c;
         }
     }

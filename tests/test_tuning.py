@@ -90,7 +90,7 @@ def test_configs_may_be_a_function_of_the_problem():
 
 @pytest.mark.parametrize("shape", [(4096, 4096, 4096), (1024, 1024, 1024), (2048, 2048, 2048), (8192, 512, 1024),
                                    (4000, 5000, 3000), (512, 512, 65536), (128, 128, 128), (1, 1, 8),
-                                   (16384, 16384, 512)])
+                                   (16384, 16384, 512), (3072, 3072, 3072), (6144, 2048, 2048)])
 @pytest.mark.parametrize("layout,dtype", [("nt", F16), ("nn", BF16)])
 def test_default_config_is_a_built_legal_configuration(shape, layout, dtype):
     M, N, K = shape
@@ -100,9 +100,13 @@ def test_default_config_is_a_built_legal_configuration(shape, layout, dtype):
     st = pg.gemm_check(0 if layout == "nt" else 1, M, N, K, dtype, c["block_M"], c["block_N"], c["block_K"],
                        c["num_stages"], c["threads"], MI355X, a_lead=c["a_lead"])
     assert st == 0, pg.last_error()
-    tiles = -(-M // c["block_M"]) * -(-N // c["block_N"])
-    if M * N >= 256 * 256 * 256:
-        assert tiles >= 256     # large problems fill the 256 compute units
+    # the cheapest of the per-tile table entries under the cost model
+    table = [dict(block_M=256, block_N=256, block_K=64, num_stages=2, a_lead=1, threads=512),
+             dict(block_M=256, block_N=128, block_K=64, num_stages=3, a_lead=0, threads=256),
+             dict(block_M=128, block_N=256, block_K=64, num_stages=3, a_lead=1, threads=256),
+             dict(block_M=128, block_N=128, block_K=64, num_stages=4, a_lead=0, threads=256)]
+    costs = pt.model_costs(M, N, K, table)
+    assert c == table[min(range(4), key=lambda i: (costs[i], i))]
 
 
 def test_default_config_of_the_headline_problem():
