@@ -38,12 +38,14 @@ extern "C" {
  *              accumulation; P is rounded to dtype for the second product
  *   is_causal  1: query i sees keys j <= i (needs seq_q == seq_kv)
  *   scale      softmax scale; 0 selects 1 / sqrt(dim)
- *   block_M    queries per workgroup, 32 per wave (threads = 2 x block_M)
+ *   block_M    queries per workgroup, 32 or 64 per wave (threads = 2 x block_M
+ *              or block_M); built: (block_M, block_N, threads) = (128, 64, 256),
+ *              (256, 64, 512), (128, 128, 256), (256, 64, 256)
  *   block_N    keys per LDS tile: 64 or 128
  *   num_stages LDS ring slots, each holding one K and one V tile
  *              (num_stages x 2 x block_N x dim x 2 bytes of LDS); 1 = single
  *              buffer; 0 = alias of 1
- *   threads    64 x waves (0 selects 2 x block_M)
+ *   threads    64 x waves (0 selects 2 x block_M, i.e. 32 queries per wave)
  * Returns a gemm_status (pipegemm.h).
  */
 int attn_fwd(const void *Q, const void *K, const void *V, void *O, int64_t batch, int64_t heads, int64_t kv_heads,

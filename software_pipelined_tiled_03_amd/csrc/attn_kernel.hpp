@@ -1,14 +1,15 @@
 // Device code of the pipelined attention forward pass (gfx950 / MI355X).
 //
 // O = softmax(scale * Q K^T [causal mask]) V for one (batch, head) and a block
-// of BM = 32 * WAVES queries per workgroup.  The KV-length loop is the long
+// of BM = 32 * QB * WAVES queries per workgroup (QB blocks of 32 per wave).  The KV-length loop is the long
 // reduction loop the TileLang tutorial pipelines exactly like the GEMM K loop
 // (chapter 11, section 1.4): the K and V tiles of BN keys stream from HBM into
 // a ring of S LDS slots with direct-to-LDS loads, copies of later tiles in
 // flight while the matrix cores work on the current one (section 2.3: versioned
 // buffers; section 5.2: a slot is refilled only after its last reader is done).
 //
-// Per wave (32 queries) and K/V tile:
+// Per wave (QB blocks of 32 queries; every K and V fragment read from LDS feeds
+// QB MFMAs, so a second block halves the LDS reads per flop) and K/V tile:
 //   S^T = K Q^T        v_mfma_f32_32x32x16 with the K fragment first, so each
 //                      lane ends with one query's scores for 16 of every 32
 //                      keys (its partner lane l ^ 32 holds the other 16);
@@ -44,9 +45,9 @@ struct AttnArgs {
     int nq;            // ceil(Sq / BM)
 };
 
-template <int BN_, int WAVES_>
+template <int BN_, int WAVES_, int QB_ = 1>
 struct AttnTile {
-    static constexpr int D = 128, BN = BN_, WAVES = WAVES_, BM = 32 * WAVES, THREADS = 64 * WAVES;
+    static constexpr int D = 128, BN = BN_, WAVES = WAVES_, QB = QB_, BM = 32 * QB * WAVES, THREADS = 64 * WAVES;
     static constexpr int K_BYTES = BN * D * 2, V_BYTES = BN * D * 2, SLOT_BYTES = K_BYTES + V_BYTES;
     static constexpr int K_LOADS = K_BYTES / (1024 * WAVES), V_LOADS = V_BYTES / (1024 * WAVES);
     static constexpr int LOADS = K_LOADS + V_LOADS;
@@ -55,6 +56,7 @@ struct AttnTile {
     static constexpr int DB = D / 32;   // 32-wide d blocks of O^T
     static constexpr int KS = BN / 16;  // 16-key steps of O^T
     static_assert(BN == 64 || BN == 128, "block_N must be 64 or 128");
+    static_assert(QB == 1 || QB == 2, "one or two 32-query blocks per wave");
     static_assert(K_BYTES % (1024 * WAVES) == 0 && K_LOADS >= 1, "whole 1 KiB copies per wave");
 };
 
@@ -64,7 +66,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
     using E = Elem<T>;
     using frag = typename E::frag;
     constexpr int D = Cfg::D, BN = Cfg::BN, BM = Cfg::BM, WAVES = Cfg::WAVES;
-    constexpr int KB = Cfg::KB, DS = Cfg::DS, DB = Cfg::DB, KS = Cfg::KS;
+    constexpr int KB = Cfg::KB, DS = Cfg::DS, DB = Cfg::DB, KS = Cfg::KS, QB = Cfg::QB;
 
     extern __shared__ __attribute__((aligned(1024))) char smem[];
 
@@ -80,8 +82,8 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
     const int b = bh / p.H, h = bh % p.H;
     const int hk = h / p.groups;
     const int q0 = qblk * BM;
-    const int q0w = q0 + wave * 32;  // this wave's first query
-    const int qi = q0w + lr;         // this lane's query (column of S^T and O^T)
+    const int q0w = q0 + wave * 32 * QB;  // this wave's first query
+    // this lane's query in block qb (column of S^T and O^T): q0w + 32 qb + lr
     const int Skv = p.Skv;
 
     // key tiles: all of them, or up to the block's last query with the mask
@@ -93,16 +95,19 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
     const char *vbase = (const char *)p.V + (size_t)(b * p.Hkv + hk) * Skv * (D * 2);
     const int kv_bytes = Skv * D * 2;
 
-    // Q fragments, second operand of S^T = K Q^T: lane l holds query qi,
-    // d = 16 ds + 8 lh .. +7.  Queries past Sq read as zero.
-    frag qf[DS];
+    // Q fragments, second operand of S^T = K Q^T: lane l holds query
+    // q0w + 32 qb + lr, d = 16 ds + 8 lh .. +7.  Queries past Sq read as zero.
+    frag qf[QB][DS];
     {
         const __amdgpu_buffer_rsrc_t rq =
             __builtin_amdgcn_make_buffer_rsrc((void *)qbase, 0, p.Sq * D * 2, 0x00020000);
 #pragma unroll
-        for (int ds = 0; ds < DS; ++ds)
-            qf[ds] = __builtin_bit_cast(
-                frag, __builtin_amdgcn_raw_buffer_load_b128(rq, (uint32_t)(qi * D * 2 + (16 * ds + 8 * lh) * 2), 0, 0));
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds)
+                qf[qb][ds] = __builtin_bit_cast(
+                    frag, __builtin_amdgcn_raw_buffer_load_b128(
+                              rq, (uint32_t)((q0w + 32 * qb + lr) * D * 2 + (16 * ds + 8 * lh) * 2), 0, 0));
     }
 
     // Copies: per-lane offsets within a tile; each tile goes through a buffer
@@ -169,14 +174,21 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
         }
     };
 
-    // Accumulators and softmax state (for query qi; the partner lane holds the same).
-    f32x16 oacc[DB];
+    // Accumulators and softmax state (per query block; the partner lane holds the same).
+    f32x16 oacc[DB][QB];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-            oacc[db][v] = 0.0f;
-    float m_run = -INFINITY, l_run = 0.0f;
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                oacc[db][qb][v] = 0.0f;
+    float m_run[QB], l_run[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+        m_run[qb] = -INFINITY;
+        l_run[qb] = 0.0f;
+    }
     const float sl2 = p.scale_log2;
 
     // One key tile j in `slot`: S^T, softmax, O^T.  The copies of tile cj into
@@ -184,12 +196,14 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
     // S^T k-steps, V pieces among the O^T k-steps.
     auto compute_tile = [&](int j, const char *slot, int cj, char *cslot, auto copies_c) __attribute__((always_inline)) {
         constexpr bool copies = decltype(copies_c)::value;
-        f32x16 sacc[KB];
+        f32x16 sacc[KB][QB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-                sacc[kb][v] = 0.0f;
+            for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    sacc[kb][qb][v] = 0.0f;
         frag kf[2][KB];
         read_k(slot, 0, kf[0]);
         static_for<DS>([&](auto ds_c) __attribute__((always_inline)) {
@@ -201,7 +215,9 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
                 issue_k(cj, cslot, c0, c1);
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
-                sacc[kb] = E::mfma(kf[ds & 1][kb], qf[ds], sacc[kb]);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    sacc[kb][qb] = E::mfma(kf[ds & 1][kb], qf[qb][ds], sacc[kb][qb]);
         });
 
         // mask: keys past the query (causal) or past Skv
@@ -210,41 +226,47 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int key = key0 + 32 * kb + 8 * (v >> 2) + 4 * lh + (v & 3);
-                    if ((p.causal && key > qi) || key >= Skv)
-                        sacc[kb][v] = -INFINITY;
-                }
+                for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int key = key0 + 32 * kb + 8 * (v >> 2) + 4 * lh + (v & 3);
+                        if ((p.causal && key > q0w + 32 * qb + lr) || key >= Skv)
+                            sacc[kb][qb][v] = -INFINITY;
+                    }
         }
-        // online softmax (base-2 exponentials of scale x log2(e) x score)
-        float mx = sacc[0][0];
+        // online softmax per query block (base-2 exponentials of
+        // scale x log2(e) x score)
+        frag pf[KS][QB];
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int qb = 0; qb < QB; ++qb) {
+            float mx = sacc[0][qb][0];
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-                mx = fmaxf(mx, sacc[kb][v]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float m_new = fmaxf(m_run, mx);  // finite: every query sees key 0 in tile 0
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * sl2);
-        const float mb = m_new * sl2;
-        float rs = 0.0f;
-        frag pf[KS];
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+                for (int v = 0; v < 16; ++v)
+                    mx = fmaxf(mx, sacc[kb][qb][v]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32));
+            const float m_new = fmaxf(m_run[qb], mx);  // finite: every query sees key 0 in tile 0
+            const float alpha = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * sl2);
+            const float mb = m_new * sl2;
+            float rs = 0.0f;
 #pragma unroll
-            for (int jj = 0; jj < 8; ++jj) {
-                const float e = __builtin_amdgcn_exp2f(fmaf(sacc[ks >> 1][8 * (ks & 1) + jj], sl2, -mb));
-                rs += e;
-                pf[ks][jj] = (T)e;
-            }
-        rs += __shfl_xor(rs, 32);
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+                for (int jj = 0; jj < 8; ++jj) {
+                    const float e = __builtin_amdgcn_exp2f(fmaf(sacc[ks >> 1][qb][8 * (ks & 1) + jj], sl2, -mb));
+                    rs += e;
+                    pf[ks][qb][jj] = (T)e;
+                }
+            rs += __shfl_xor(rs, 32);
+            l_run[qb] = l_run[qb] * alpha + rs;
+            m_run[qb] = m_new;
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-                oacc[db][v] *= alpha;
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    oacc[db][qb][v] *= alpha;
+        }
 
         // O^T += V^T P^T
         frag vf[2][DB];
@@ -259,7 +281,9 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
                 issue_v(cj, cslot, c0, c1);
 #pragma unroll
             for (int db = 0; db < DB; ++db)
-                oacc[db] = E::mfma(vf[ks & 1][db], pf[ks], oacc[db]);
+#pragma unroll
+                for (int qb = 0; qb < QB; ++qb)
+                    oacc[db][qb] = E::mfma(vf[ks & 1][db], pf[ks][qb], oacc[db][qb]);
         });
         // every LDS read of this slot has returned
         wait_lds();
@@ -321,30 +345,33 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
     wait_vmcnt<0>();
     barrier();
     char *strip = smem + wave * 2048 * G;
-    const float inv_l = 1.0f / l_run;
     short *obase = (short *)((char *)p.O + (size_t)(b * p.H + h) * p.Sq * (D * 2));
 #pragma unroll
-    for (int gp = 0; gp < DB / G; ++gp) {
+    for (int qb = 0; qb < QB; ++qb) {
+        const float inv_l = 1.0f / l_run[qb];
 #pragma unroll
-        for (int gb = 0; gb < G; ++gb)
+        for (int gp = 0; gp < DB / G; ++gp) {
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                typename E::quad v;
+            for (int gb = 0; gb < G; ++gb)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    v[r] = (T)(oacc[gp * G + gb][4 * q + r] * inv_l);
-                *(typename E::quad *)(strip + cbuf_half_offset(lr, 4 * gb + q, lh, G)) = v;
+                for (int q = 0; q < 4; ++q) {
+                    typename E::quad v;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        v[r] = (T)(oacc[gp * G + gb][qb][4 * q + r] * inv_l);
+                    *(typename E::quad *)(strip + cbuf_half_offset(lr, 4 * gb + q, lh, G)) = v;
+                }
+#pragma unroll
+            for (int i = 0; i < 2 * G; ++i) {
+                const int idx = i * 64 + lane;
+                const int r = idx / CH, c = idx % CH;
+                i16x8 x = *(const i16x8 *)(strip + cbuf_chunk_offset(r, c, G));
+                if (hswz(r))
+                    x = __builtin_shufflevector(x, x, 4, 5, 6, 7, 0, 1, 2, 3);
+                const int query = q0w + 32 * qb + r;
+                if (query < p.Sq)
+                    *(i16x8 *)(obase + (size_t)query * D + (gp * G) * 32 + c * 8) = x;
             }
-#pragma unroll
-        for (int i = 0; i < 2 * G; ++i) {
-            const int idx = i * 64 + lane;
-            const int r = idx / CH, c = idx % CH;
-            i16x8 x = *(const i16x8 *)(strip + cbuf_chunk_offset(r, c, G));
-            if (hswz(r))
-                x = __builtin_shufflevector(x, x, 4, 5, 6, 7, 0, 1, 2, 3);
-            const int query = q0w + r;
-            if (query < p.Sq)
-                *(i16x8 *)(obase + (size_t)query * D + (gp * G) * 32 + c * 8) = x;
         }
     }
 }

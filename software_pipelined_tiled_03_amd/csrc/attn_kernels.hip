@@ -10,10 +10,10 @@
 
 namespace pipegemm {
 
-template <class T, int BN, int WAVES>
+template <class T, int BN, int WAVES, int QB>
 hipError_t attn_launch(const AttnArgs &args, int grid, int lds_bytes, hipStream_t stream)
 {
-    using Cfg = AttnTile<BN, WAVES>;
+    using Cfg = AttnTile<BN, WAVES, QB>;
     static std::once_flag once;
     static hipError_t attr_err = hipSuccess;
     std::call_once(once, [] {
@@ -26,8 +26,8 @@ hipError_t attn_launch(const AttnArgs &args, int grid, int lds_bytes, hipStream_
     return hipGetLastError();
 }
 
-#define PG_ATTN_INSTANTIATE(BN, W) \
-    template hipError_t attn_launch<PG_ELEM, BN, W>(const AttnArgs &, int, int, hipStream_t);
+#define PG_ATTN_INSTANTIATE(BN, W, QB) \
+    template hipError_t attn_launch<PG_ELEM, BN, W, QB>(const AttnArgs &, int, int, hipStream_t);
 PG_ATTN_TILE_LIST(PG_ATTN_INSTANTIATE)
 #undef PG_ATTN_INSTANTIATE
 

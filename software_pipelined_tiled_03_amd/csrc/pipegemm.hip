@@ -327,14 +327,14 @@ double model_cost_us(const gemm_config &c, int64_t M, int64_t N, int64_t K)
 typedef hipError_t (*attn_launch_fn)(const AttnArgs &, int grid, int lds_bytes, hipStream_t);
 
 struct AttnInstance {
-    int dtype, bn, waves;
+    int dtype, bn, waves, qb;  // qb: 32-query blocks per wave
     int loads_per_wave;  // 1 KiB copies per wave per K/V tile pair
     attn_launch_fn launch;
 };
 
-#define PG_ATTN_ROW(DT, T, BN, W) {DT, BN, W, 2 * BN * 128 * 2 / (1024 * W), &attn_launch<T, BN, W>},
-#define PG_ATTN_ROW_F16(BN, W) PG_ATTN_ROW(GEMM_F16, _Float16, BN, W)
-#define PG_ATTN_ROW_BF16(BN, W) PG_ATTN_ROW(GEMM_BF16, __bf16, BN, W)
+#define PG_ATTN_ROW(DT, T, BN, W, QB) {DT, BN, W, QB, 2 * BN * 128 * 2 / (1024 * W), &attn_launch<T, BN, W, QB>},
+#define PG_ATTN_ROW_F16(BN, W, QB) PG_ATTN_ROW(GEMM_F16, _Float16, BN, W, QB)
+#define PG_ATTN_ROW_BF16(BN, W, QB) PG_ATTN_ROW(GEMM_BF16, __bf16, BN, W, QB)
 const AttnInstance kAttnInstances[] = {PG_ATTN_TILE_LIST(PG_ATTN_ROW_F16) PG_ATTN_TILE_LIST(PG_ATTN_ROW_BF16)};
 
 int64_t attn_lds_of(int bn, int dim, int stages)
@@ -380,13 +380,16 @@ int attn_validate(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Skv, in
     // (4) supported configuration and size limits
     if (D != 128)
         return fail(GEMM_ERR_UNSUPPORTED, "attention is built for dim 128 (got %lld)", (long long)D);
+    // block_M = 32 x (query blocks per wave) x waves; threads 0 = one block per wave
     const int th = threads == 0 ? 2 * bm : threads;
-    if (bm % 32 != 0 || th != 2 * bm)
-        return fail(GEMM_ERR_UNSUPPORTED, "block_M must be 32 per wave with threads = 2 x block_M (got %d, %d)", bm,
-                    th);
+    const int waves = th / 64;
+    if (waves < 1 || bm % (32 * waves) != 0)
+        return fail(GEMM_ERR_UNSUPPORTED,
+                    "block_M must be 32 or 64 queries per wave (got block_M %d with %d threads)", bm, th);
+    const int qb = bm / (32 * waves);
     const AttnInstance *in = nullptr;
     for (const AttnInstance &a : kAttnInstances)
-        if (a.dtype == dtype && a.bn == bn && a.waves == th / 64)
+        if (a.dtype == dtype && a.bn == bn && a.waves == waves && a.qb == qb)
             in = &a;
     if (!in)
         return fail(GEMM_ERR_UNSUPPORTED, "no attention kernel built for block_M %d, block_N %d", bm, bn);

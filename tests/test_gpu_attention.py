@@ -16,7 +16,8 @@ pytestmark = pytest.mark.gpu
 
 F16, BF16 = inputs.F16, inputs.BF16
 TORCH_DT = {F16: torch.float16, BF16: torch.bfloat16}
-TILES = [(128, 64, 256), (256, 64, 512), (128, 128, 256)]   # (block_M, block_N, threads)
+# (block_M, block_N, threads); 256 queries on 256 threads = two 32-query blocks per wave
+TILES = [(128, 64, 256), (256, 64, 512), (128, 128, 256), (256, 64, 256)]
 
 
 def dev(u16, dtype):
@@ -78,12 +79,13 @@ def test_explicit_scale():
     assert_close(run(w, Q, K, V, (256, 64, 512), 3, scale=0.3), want, BF16, "scale 0.3")
 
 
+@pytest.mark.parametrize("tile", [(128, 64, 256), (256, 64, 256)], ids=lambda t: "bm%d_bn%d_t%d" % t)
 @pytest.mark.parametrize("name", ["attn_f16_b4_h32_s4096_d128", "attn_f16_b4_h32_s4096_d128_causal",
                                   "attn_bf16_b2_h32_kv8_s2048_d128_causal"])
-def test_full_size_sampled_rows(name):
+def test_full_size_sampled_rows(name, tile):
     w = inputs.attention_workload(name)
     Q, K, V = w.make()
-    got = run(w, Q, K, V, (128, 64, 256), 2)
+    got = run(w, Q, K, V, tile, 2)
     rng = np.random.default_rng(11)
     for b, h in [(0, 0), (w.batch - 1, w.heads - 1), (w.batch // 2, 5)]:
         rows = np.unique(np.concatenate([[0, 1, 127, 128, w.seq_q - 1], rng.integers(0, w.seq_q, 8)]))
