@@ -132,6 +132,30 @@ def time_gemm(fn, dA, dB, C, block, stages, threads, steps, warmup, a_lead=0, re
     return start.elapsed_time(end) / steps
 
 
+def launch_distribution(fn, dA, dB, C, block, stages, threads, a_lead=0, reps=100, warmup=25, scrub=None):
+    """Per-launch durations (HIP events around each single launch on the
+    current stream): median, min and p90 in ms.  With `scrub` (a device byte
+    tensor larger than the last-level caches) every timed launch is preceded by
+    a write of the whole scrub buffer outside its events, so A and B start cold."""
+    import torch
+
+    for _ in range(warmup):
+        fn(dA, dB, out=C, block=block, num_stages=stages, threads=threads, a_lead=a_lead)
+    stream = torch.cuda.current_stream()
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda.synchronize()
+    for i, (e0, e1) in enumerate(pairs):
+        if scrub is not None:
+            scrub.fill_(i & 0xFF)
+        e0.record(stream)
+        fn(dA, dB, out=C, block=block, num_stages=stages, threads=threads, a_lead=a_lead)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t = sorted(e0.elapsed_time(e1) for e0, e1 in pairs)
+    return dict(median_ms=round(t[len(t) // 2], 5), min_ms=round(t[0], 5),
+                p90_ms=round(t[min(len(t) - 1, (9 * len(t)) // 10)], 5))
+
+
 def attention_sweep(steps=10, warmup=3):
     """TFLOP/s (4 B H D x visible query-key pairs / t) of the attention kernel
     per ring depth on the ATTENTION workloads."""
@@ -278,6 +302,20 @@ def main():
     _log("headline %s tile %s S=%d%s threads=%d: %.3f ms, %.1f TFLOP/s"
          % (w.name, block, stages, "+A" if a_lead else "", threads, ms, tflops))
 
+    # per-launch distribution of the same configuration, warm and with the
+    # caches scrubbed (512 MiB written between launches: twice the MALL)
+    per_launch = None
+    if not args.no_sweep:
+        warm = launch_distribution(fn, dA, dB, C, block, stages, threads, a_lead=a_lead)
+        scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        cold = launch_distribution(fn, dA, dB, C, block, stages, threads, a_lead=a_lead, scrub=scrub)
+        del scrub
+        for d in (warm, cold):
+            d["median_tflops"] = round(flops / d["median_ms"] / 1e9, 1)
+        per_launch = {"reps": 100, "warmup": 25, "warm": warm, "cold_scrub_512mib": cold}
+        _log("per launch: warm median %.4f ms (min %.4f, p90 %.4f); cold median %.4f ms"
+             % (warm["median_ms"], warm["min_ms"], warm["p90_ms"], cold["median_ms"]))
+
     attn = None if args.no_attention or args.no_sweep else attention_sweep()
 
     # the fused GEMM+ReLU epilogue in the same configuration
@@ -332,6 +370,7 @@ def main():
         "cpu_baseline": cpu,
         "per_num_stages": sweep,
         "fused_relu": {"tflops": round(flops / relu_ms / 1e9, 2), "ms_per_step": round(relu_ms, 5)},
+        "per_launch": per_launch,
         "attention": attn,
         "context_torch_matmul_tflops": ref,
     }
