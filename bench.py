@@ -32,11 +32,16 @@ SWEEPS = [
     ("tile256x256x32_t512", "nt_f16_4096", (256, 256, 32), 512, ("1", "2", "3", "4", "2+A", "3+A")),
     ("tile256x256x64_t256", "nt_f16_4096", (256, 256, 64), 256, ("1", "2", "2+A")),
     ("tile256x256x64_t512", "nt_f16_4096", (256, 256, 64), 512, ("1", "2", "2+A")),
-    ("nn_bf16_tile128x128x32_t256", "nn_bf16_4096", (128, 128, 32), 256, ("3",)),
-    ("nn_bf16_tile128x256x64_t256", "nn_bf16_4096", (128, 256, 64), 256, ("3",)),
-    ("nn_bf16_tile256x128x32_t256", "nn_bf16_4096", (256, 128, 32), 256, ("3",)),
+    ("nn_bf16_tile128x128x32_t256", "nn_bf16_4096", (128, 128, 32), 256, ("1", "2", "3", "4", "6")),
+    ("nn_bf16_tile128x256x64_t256", "nn_bf16_4096", (128, 256, 64), 256, ("1", "2", "3")),
+    ("nn_bf16_tile256x128x32_t256", "nn_bf16_4096", (256, 128, 32), 256, ("1", "2", "3", "4", "6")),
     ("nn_bf16_tile256x256x64_t256", "nn_bf16_4096", (256, 256, 64), 256, ("2", "2+A")),
     ("nn_bf16_tile256x256x64_t512", "nn_bf16_4096", (256, 256, 64), 512, ("2", "2+A")),
+    # the smaller and ragged shapes: one workgroup, 64 workgroups, ragged edges, a long K loop
+    ("cfg1_128_tile128x128x32_t256", "nt_f16_128", (128, 128, 32), 256, ("1",)),
+    ("cfg2_1024_tile128x128x32_t256", "nt_f16_1024", (128, 128, 32), 256, ("1", "2", "3")),
+    ("cfg5a_ragged_tile128x128x32_t256", "nt_f16_ragged_4000x5000x3000", (128, 128, 32), 256, ("3",)),
+    ("cfg5b_longk_tile128x128x32_t256", "nt_f16_longk_512x512x65536", (128, 128, 32), 256, ("1", "2", "3", "4", "6")),
 ]
 
 
@@ -212,6 +217,67 @@ def cpu_baseline(w, A, B, rows):
                        % (rows - 1, w.M, w.N, w.K, w.layout.upper(), flops / 1e9, dt))
 
 
+# Oracle timing table: (workload, timed runs, also on one thread)
+ORACLE_TABLE = [
+    ("nt_f16_128", 3, True),
+    ("nt_f16_1024", 3, True),
+    ("nt_f16_4096", 1, False),
+    ("nn_bf16_4096", 1, False),
+    ("nt_f16_ragged_4000x5000x3000", 1, False),
+    ("nt_f16_longk_512x512x65536", 3, True),
+]
+
+
+def oracle_table_worker(one_thread):
+    """Times the CPU oracle (whole C, every row) on each workload of
+    ORACLE_TABLE; with one_thread only on the workloads marked for it.  Runs
+    in its own process so that OMP_NUM_THREADS is read at the oracle's load."""
+    if one_thread:
+        os.environ["OMP_NUM_THREADS"] = "1"
+    from oracle import gemm as og
+    from software_pipelined_tiled_03_amd import inputs
+
+    rows = []
+    for name, runs, single in ORACLE_TABLE:
+        if one_thread and not single:
+            continue
+        w = inputs.workload(name)
+        A, B = w.make()
+        fn = og.gemm_nt if w.layout == "nt" else og.gemm_nn
+        fn(A, B, w.dtype, rows=(0, 1))
+        ts = []
+        for _ in range(runs):
+            t0 = time.perf_counter()
+            fn(A, B, w.dtype)
+            ts.append(time.perf_counter() - t0)
+        t = sorted(ts)[len(ts) // 2]
+        rows.append(dict(workload=name, threads=og.num_threads(), runs=runs, seconds=round(t, 4),
+                         gflops=round(2.0 * w.M * w.N * w.K / t / 1e9, 2)))
+        _log("oracle %s on %d thread(s): %.3f s, %.2f GFLOP/s" % (name, og.num_threads(), t, rows[-1]["gflops"]))
+    return rows
+
+
+def oracle_table():
+    """The CPU oracle's timing on every GEMM workload, on all host cores and on
+    one thread; prints one JSON line.  No GPU is used."""
+    import platform
+    import subprocess
+
+    rows = []
+    for one in (0, 1):
+        r = subprocess.run([sys.executable, os.path.abspath(__file__), "--oracle-table-worker", str(one)],
+                           capture_output=True, text=True, check=True)
+        rows += json.loads(r.stdout.strip().splitlines()[-1])
+    model = platform.processor()
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
+    print(json.dumps({"oracle_table": rows, "host": {"nproc": os.cpu_count(), "cpu_model": model}}), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,7 +294,16 @@ def main():
     ap.add_argument("--threads", type=int, default=None)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (HBM counter calibration)")
+    ap.add_argument("--oracle-table", action="store_true",
+                    help="only time the CPU oracle on every GEMM workload (all cores and one thread); no GPU")
+    ap.add_argument("--oracle-table-worker", type=int, default=None, help=argparse.SUPPRESS)
     args = ap.parse_args()
+
+    if args.oracle_table_worker is not None:
+        print(json.dumps(oracle_table_worker(bool(args.oracle_table_worker))), flush=True)
+        return 0
+    if args.oracle_table:
+        return oracle_table()
 
     if args.gpus != 1:
         print("bench.py measures one GPU only: this GEMM runs on a single MI355X; "

@@ -327,9 +327,9 @@ def test_relu_headline_configuration(oracle_gemm):
     A, B = w.make()
     rows = sample_rows(w.M, 256, 21, extra=4)
     want = np.concatenate([oracle_gemm.gemm_nt(A, B, F16, rows=(r, r + 1), relu=True) for r in rows])
-    got = run_relu("nt", A, B, F16, w.M, w.N, w.K, (256, 256, 64), 2, 256, a_lead=1)
+    got = run_relu("nt", A, B, F16, w.M, w.N, w.K, (256, 256, 64), 2, 512, a_lead=1)
     assert_close(got[rows], want, F16, oracle_gemm, "relu 4096^3 256x256x64 S=2+A")
-    plain = run("nt", A, B, F16, w.M, w.N, w.K, (256, 256, 64), 2, 256, a_lead=1)
+    plain = run("nt", A, B, F16, w.M, w.N, w.K, (256, 256, 64), 2, 512, a_lead=1)
     assert np.array_equal(got, relu_of(plain, F16, oracle_gemm))
 
 
