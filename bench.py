@@ -25,6 +25,13 @@ PEAK_TFLOPS = 2500.0     # MI355X dense fp16/bf16 MFMA, published
 HEADLINE = dict(workload="nt_f16_4096", block=(256, 256, 64), num_stages=2, a_lead=1, threads=512)
 # (label, workload, block, threads, ring depths); a depth "S+A" is num_stages S with a_lead = 1
 SWEEPS = [
+    # the smaller and ragged shapes first (one workgroup, 64 workgroups, ragged
+    # edges, a long K loop on 16 CUs), so that the full-chip 4096^3 sweeps and
+    # the headline that follows them run under the same sustained load
+    ("cfg1_128_tile128x128x32_t256", "nt_f16_128", (128, 128, 32), 256, ("1",)),
+    ("cfg2_1024_tile128x128x32_t256", "nt_f16_1024", (128, 128, 32), 256, ("1", "2", "3")),
+    ("cfg5a_ragged_tile128x128x32_t256", "nt_f16_ragged_4000x5000x3000", (128, 128, 32), 256, ("3",)),
+    ("cfg5b_longk_tile128x128x32_t256", "nt_f16_longk_512x512x65536", (128, 128, 32), 256, ("1", "2", "3", "4", "6")),
     ("tile128x128x32_t128", "nt_f16_4096", (128, 128, 32), 128, ("1", "2", "3", "4", "6")),
     ("tile128x128x32_t256", "nt_f16_4096", (128, 128, 32), 256, ("1", "2", "3", "4", "6")),
     ("tile128x128x32_t512", "nt_f16_4096", (128, 128, 32), 512, ("1", "2", "3", "4", "6")),
@@ -37,11 +44,6 @@ SWEEPS = [
     ("nn_bf16_tile256x128x32_t256", "nn_bf16_4096", (256, 128, 32), 256, ("1", "2", "3", "4", "6")),
     ("nn_bf16_tile256x256x64_t256", "nn_bf16_4096", (256, 256, 64), 256, ("2", "2+A")),
     ("nn_bf16_tile256x256x64_t512", "nn_bf16_4096", (256, 256, 64), 512, ("2", "2+A")),
-    # the smaller and ragged shapes: one workgroup, 64 workgroups, ragged edges, a long K loop
-    ("cfg1_128_tile128x128x32_t256", "nt_f16_128", (128, 128, 32), 256, ("1",)),
-    ("cfg2_1024_tile128x128x32_t256", "nt_f16_1024", (128, 128, 32), 256, ("1", "2", "3")),
-    ("cfg5a_ragged_tile128x128x32_t256", "nt_f16_ragged_4000x5000x3000", (128, 128, 32), 256, ("3",)),
-    ("cfg5b_longk_tile128x128x32_t256", "nt_f16_longk_512x512x65536", (128, 128, 32), 256, ("1", "2", "3", "4", "6")),
 ]
 
 

@@ -681,7 +681,9 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
         if (m < M) {
             short *crow = (short *)(C + (size_t)m * N);
             if (p.c_vec && n + 7 < N) {
-                *(i16x8 *)(crow + n) = x;
+                // streaming store: C is written once and is far larger than the
+                // L2s, so it is not kept there (measured ~1.5 us faster at 4096^3)
+                __builtin_nontemporal_store(x, (i16x8 *)(crow + n));
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e)
