@@ -16,7 +16,8 @@ KERNEL_SRC = os.path.join(CSRC, "pipegemm_kernels.hip")
 ATTN_SRC = os.path.join(CSRC, "attn_kernels.hip")
 HOST_SRC = os.path.join(CSRC, "pipegemm.hip")
 DEPS = [KERNEL_SRC, ATTN_SRC, HOST_SRC] + [os.path.join(CSRC, f) for f in (
-    "pipegemm_kernel.hpp", "pipegemm_launch.hpp", "pipegemm_layout.hpp", "attn_kernel.hpp", "attn_launch.hpp")] + [
+    "pipegemm_kernel.hpp", "pipegemm_launch.hpp", "pipegemm_layout.hpp", "attn_kernel.hpp", "attn_launch.hpp",
+    "launch_util.hpp")] + [
     os.path.join(ROOT, "include", f) for f in ("pipegemm.h", "pipeattn.h")]
 # one kernel translation unit per (element type, B layout, K bound), compiled in parallel
 VARIANTS = [("%s_%s_k%d" % (n, l, kc), e, nn, kc)

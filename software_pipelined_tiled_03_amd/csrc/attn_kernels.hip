@@ -1,8 +1,7 @@
 // Attention kernel instantiations for one element type (PG_ELEM).
 #include "attn_kernel.hpp"
 #include "attn_launch.hpp"
-
-#include <mutex>
+#include "launch_util.hpp"
 
 #ifndef PG_ELEM
 #error "PG_ELEM must name the element type"
@@ -14,12 +13,8 @@ template <class T, int BN, int WAVES, int QB>
 hipError_t attn_launch(const AttnArgs &args, int grid, int lds_bytes, hipStream_t stream)
 {
     using Cfg = AttnTile<BN, WAVES, QB>;
-    static std::once_flag once;
-    static hipError_t attr_err = hipSuccess;
-    std::call_once(once, [] {
-        attr_err = hipFuncSetAttribute((const void *)&attn_kernel<T, Cfg>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       160 * 1024);
-    });
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t attr_err = allow_full_lds((const void *)&attn_kernel<T, Cfg>, lds_set);
     if (attr_err != hipSuccess)
         return attr_err;
     hipLaunchKernelGGL((attn_kernel<T, Cfg>), dim3(grid), dim3(Cfg::THREADS), lds_bytes, stream, args);

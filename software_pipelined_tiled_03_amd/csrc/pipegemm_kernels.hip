@@ -2,9 +2,8 @@
 // selected by PG_ELEM (_Float16 or __bf16), PG_NN (0 = NT, 1 = NN) and
 // PG_KCHECK (1 = the per-chunk K bound of a ragged last K tile) at compile time.
 #include "pipegemm_kernel.hpp"
+#include "launch_util.hpp"
 #include "pipegemm_launch.hpp"
-
-#include <mutex>
 
 #ifndef PG_ELEM
 #error "PG_ELEM must name the element type"
@@ -22,12 +21,8 @@ template <class T, bool NN, int BM, int BN, int BK, int WM, int WN, bool KCHECK>
 hipError_t launch(const KernelArgs &args, int grid, int lds_bytes, hipStream_t stream)
 {
     using Cfg = Tile<BM, BN, BK, WM, WN>;
-    static std::once_flag once;
-    static hipError_t attr_err = hipSuccess;
-    std::call_once(once, [] {
-        attr_err = hipFuncSetAttribute((const void *)&gemm_kernel<T, NN, Cfg, KCHECK>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
-    });
+    static std::atomic<uint64_t> lds_set{0};
+    const hipError_t attr_err = allow_full_lds((const void *)&gemm_kernel<T, NN, Cfg, KCHECK>, lds_set);
     if (attr_err != hipSuccess)
         return attr_err;
     hipLaunchKernelGGL((gemm_kernel<T, NN, Cfg, KCHECK>), dim3(grid), dim3(Cfg::THREADS), lds_bytes, stream, args);
