@@ -157,6 +157,8 @@ def _gemm(layout, A, B, out, block, num_stages, threads, stream, a_lead, relu=Fa
         raise GemmArgumentError(GEMM_ERR_ARG, "A and B must be 2-D")
     if not (A.is_cuda and B.is_cuda):
         raise GemmArgumentError(GEMM_ERR_ARG, "A and B must be device tensors")
+    if A.device != B.device:
+        raise GemmArgumentError(GEMM_ERR_ARG, "A and B are on different devices (%s, %s)" % (A.device, B.device))
     if not (A.is_contiguous() and B.is_contiguous()):
         raise GemmArgumentError(GEMM_ERR_ARG, "A and B must be contiguous row-major")
     if A.dtype != B.dtype:
@@ -247,6 +249,8 @@ def attention(Q, K, V, causal=False, scale=0.0, out=None, block_M=128, block_N=6
         raise GemmArgumentError(GEMM_ERR_ARG, "Q, K and V must be 4-D [batch, heads, seq, dim]")
     if not (Q.is_cuda and K.is_cuda and V.is_cuda):
         raise GemmArgumentError(GEMM_ERR_ARG, "Q, K and V must be device tensors")
+    if not (Q.device == K.device == V.device):
+        raise GemmArgumentError(GEMM_ERR_ARG, "Q, K and V are not all on one device")
     if not (Q.is_contiguous() and K.is_contiguous() and V.is_contiguous()):
         raise GemmArgumentError(GEMM_ERR_ARG, "Q, K and V must be contiguous")
     if not (Q.dtype == K.dtype == V.dtype):
