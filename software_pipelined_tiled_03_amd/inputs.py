@@ -77,7 +77,7 @@ class Workload:
         return 2 * self.M * self.N * self.K
 
 
-#: The five measured workloads (the fifth in two shapes).
+#: The five measured workloads (the fifth in two shapes), and one GPU's share of the third.
 WORKLOADS = {
     "nt_f16_128": Workload("nt_f16_128", "nt", F16, 128, 128, 128, 1000, 1001),
     "nt_f16_1024": Workload("nt_f16_1024", "nt", F16, 1024, 1024, 1024, 2000, 2001),
@@ -87,6 +87,10 @@ WORKLOADS = {
                                              5000, 5001),
     "nt_f16_longk_512x512x65536": Workload("nt_f16_longk_512x512x65536", "nt", F16, 512, 512, 65536,
                                            5100, 5101),
+    # one GPU's share of the 4096^3 problem split over 8 GPUs along M: the
+    # same seeds draw A row by row, so A here is rows 0..511 of that A
+    "nt_f16_shard8_512x4096x4096": Workload("nt_f16_shard8_512x4096x4096", "nt", F16, 512, 4096, 4096,
+                                            3000, 3001),
 }
 
 

@@ -165,6 +165,24 @@ def test_long_k_512x512x65536(oracle_gemm):
     assert_close(got[rows], want, F16, oracle_gemm, "long K 256x256x64 S=2 a_lead")
 
 
+def test_one_gpu_share_512x4096x4096(oracle_gemm):
+    # rows 0..511 of the 4096^3 problem, in the configurations the bench sweeps;
+    # in the headline configuration the share is bit for bit the same rows of
+    # the whole product (a C tile does not depend on the tiles beside it)
+    w = inputs.workload("nt_f16_shard8_512x4096x4096")
+    A, B = w.make()
+    rows = sample_rows(w.M, 128, 7, extra=4)
+    want = oracle_rows(oracle_gemm, "nt", A, B, F16, rows)
+    for block, s, th, lead in (((128, 128, 64), 3, 256, 0), ((128, 128, 32), 3, 512, 0), ((128, 256, 64), 2, 256, 0),
+                               ((256, 256, 64), 2, 512, 1)):
+        got = run("nt", A, B, F16, w.M, w.N, w.K, block, s, th, a_lead=lead)
+        assert_close(got[rows], want, F16, oracle_gemm, "shard %s S=%d threads=%d" % (block, s, th))
+    full = inputs.workload("nt_f16_4096")
+    Af, Bf = full.make()
+    whole = run("nt", Af, Bf, F16, full.M, full.N, full.K, (256, 256, 64), 2, 512, a_lead=1)
+    assert np.array_equal(got, whole[:512]), "the share differs from the same rows of the whole product"
+
+
 # --------------------------------------------------------------------------
 # Every built tile, both layouts and dtypes, on a shape ragged in M, N and K
 
