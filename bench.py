@@ -30,9 +30,11 @@ SWEEPS = [
     # the headline that follows them run under the same sustained load
     ("cfg1_128_tile128x128x32_t256", "nt_f16_128", (128, 128, 32), 256, ("1",)),
     ("cfg2_1024_tile128x128x32_t256", "nt_f16_1024", (128, 128, 32), 256, ("1", "2", "3")),
+    ("cfg2_1024_tile64x128x64_t256", "nt_f16_1024", (64, 128, 64), 256, ("2", "3", "4")),
     ("cfg5a_ragged_tile128x128x32_t256", "nt_f16_ragged_4000x5000x3000", (128, 128, 32), 256, ("3",)),
     ("cfg5b_longk_tile128x128x32_t256", "nt_f16_longk_512x512x65536", (128, 128, 32), 256, ("1", "2", "3", "4", "6")),
-    # one GPU's share of 4096^3 over 8 GPUs (512 x 4096 x 4096): 128 or 32 workgroups
+    # one GPU's share of 4096^3 over 8 GPUs (512 x 4096 x 4096): 256, 128 or 32 workgroups
+    ("shard8_tile64x128x64_t256", "nt_f16_shard8_512x4096x4096", (64, 128, 64), 256, ("2", "3", "4", "6")),
     ("shard8_tile128x128x64_t256", "nt_f16_shard8_512x4096x4096", (128, 128, 64), 256, ("2", "3", "4")),
     ("shard8_tile128x128x32_t512", "nt_f16_shard8_512x4096x4096", (128, 128, 32), 512, ("2", "3", "4")),
     ("shard8_tile128x256x64_t256", "nt_f16_shard8_512x4096x4096", (128, 256, 64), 256, ("2", "3")),

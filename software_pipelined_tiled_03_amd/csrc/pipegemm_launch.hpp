@@ -27,6 +27,7 @@ constexpr int loads_per_wave(int bm, int bn, int bk, int waves)
 
 // The built tile shapes: X(block_M, block_N, block_K, waves along M, waves along N).
 #define PG_TILE_LIST(X)            \
+    X(64, 128, 64, 2, 2)           \
     X(128, 128, 32, 2, 1)          \
     X(128, 128, 32, 2, 2)          \
     X(128, 128, 32, 2, 4)          \

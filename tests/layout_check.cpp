@@ -468,6 +468,7 @@ int main()
 {
     check_k_tile<32>(256);
     check_k_tile<64>(256);
+    check_k_tile<64>(64);
     check_n_tile<128>(32);
     check_n_tile<128>(64);
     check_n_tile<256>(32);
