@@ -599,6 +599,7 @@ int gemm_default_config(int layout, int64_t M, int64_t N, int64_t K, int dtype, 
         {256, 128, 64, 3, 0, 256},
         {128, 256, 64, 3, 1, 256},
         {128, 128, 64, 4, 0, 256},
+        {64, 128, 64, 6, 0, 256},
     };
     const gemm_config *pick = &kTable[0];
     double best = pipegemm::model_cost_us(kTable[0], M, N, K);

@@ -104,9 +104,10 @@ def test_default_config_is_a_built_legal_configuration(shape, layout, dtype):
     table = [dict(block_M=256, block_N=256, block_K=64, num_stages=2, a_lead=1, threads=512),
              dict(block_M=256, block_N=128, block_K=64, num_stages=3, a_lead=0, threads=256),
              dict(block_M=128, block_N=256, block_K=64, num_stages=3, a_lead=1, threads=256),
-             dict(block_M=128, block_N=128, block_K=64, num_stages=4, a_lead=0, threads=256)]
+             dict(block_M=128, block_N=128, block_K=64, num_stages=4, a_lead=0, threads=256),
+             dict(block_M=64, block_N=128, block_K=64, num_stages=6, a_lead=0, threads=256)]
     costs = pt.model_costs(M, N, K, table)
-    assert c == table[min(range(4), key=lambda i: (costs[i], i))]
+    assert c == table[min(range(len(table)), key=lambda i: (costs[i], i))]
 
 
 def test_default_config_of_the_headline_problem():
@@ -114,6 +115,9 @@ def test_default_config_of_the_headline_problem():
                                                              a_lead=1, threads=512)
     assert pg.default_config("nt", 8192, 8192, 1024)["threads"] == 512
     assert pg.default_config("nt", 2048, 2048, 2048)["block_M"] == 128
+    # the small grids (1024^3, long K on a 512 x 512 C) take the 64 x 128 tile
+    assert pg.default_config("nt", 1024, 1024, 1024)["block_M"] == 64
+    assert pg.default_config("nt", 512, 512, 65536)["block_M"] == 64
 
 
 # ---------------------------------------------------------------------------
