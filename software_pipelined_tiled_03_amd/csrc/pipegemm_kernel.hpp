@@ -39,7 +39,11 @@
 //    its second, so it produces C^T blocks: each lane then holds 4 consecutive
 //    columns of one row of C;
 //  - out-of-range rows and K/N chunks read as zero through the buffer
-//    resource's range check (an offset at or beyond num_records returns 0).
+//    resource's range check (an offset at or beyond num_records returns 0);
+//  - 8-wave 256 x 256 tiles put two waves on each SIMD; a wave lowers its
+//    priority (s_setprio) only for the stretch that ends in the wait for the
+//    next tile, so its SIMD partner keeps the matrix core busy meanwhile;
+//  - C leaves through an LDS strip per wave as 16-byte streaming stores.
 #pragma once
 
 #include <hip/hip_runtime.h>
