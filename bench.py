@@ -62,6 +62,8 @@ def parse_depth(d):
 ATTENTION = [
     ("attn_f16_b4_h32_s4096_d128", (256, 64, 512), (1, 2, 3, 4)),
     ("attn_f16_b4_h32_s4096_d128_causal", (256, 64, 512), (1, 2, 3, 4)),
+    ("attn_f16_b4_h32_s4096_d128", (256, 128, 512), (1, 2)),
+    ("attn_f16_b4_h32_s4096_d128_causal", (256, 128, 512), (1, 2)),
     ("attn_f16_b4_h32_s4096_d128", (128, 64, 256), (1, 2, 3, 4)),
     ("attn_f16_b4_h32_s4096_d128", (256, 64, 256), (1, 2, 3, 4)),
     ("attn_f16_b4_h32_s4096_d128_causal", (256, 64, 256), (1, 2, 3, 4)),

@@ -20,6 +20,7 @@ constexpr int kAttnMaxStages = 4;
     X(64, 4, 1)              \
     X(64, 8, 1)              \
     X(128, 4, 1)             \
+    X(128, 8, 1)             \
     X(64, 4, 2)
 
 }  // namespace pipegemm

@@ -59,7 +59,8 @@ def test_alignment_and_unsupported():
     assert check(D=60) == pg.GEMM_ERR_ALIGN
     assert check(D=64) == pg.GEMM_ERR_UNSUPPORTED
     assert check(bm=128, th=512) == pg.GEMM_ERR_UNSUPPORTED     # threads must be 2 x block_M
-    assert check(bm=256, th=512, bn=128) == pg.GEMM_ERR_UNSUPPORTED   # not built
+    assert check(bm=256, th=256, bn=128) == pg.GEMM_ERR_UNSUPPORTED   # not built (two blocks per wave, 128 keys)
+    assert check(bm=256, th=512, bn=128) == pg.GEMM_OK
     assert check(bm=256, th=512, bn=64) == pg.GEMM_OK
     assert check(bm=256, th=0, bn=64) == pg.GEMM_OK             # default threads = 2 x block_M
     assert check(bn=32) == pg.GEMM_ERR_UNSUPPORTED

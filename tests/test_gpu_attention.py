@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 F16, BF16 = inputs.F16, inputs.BF16
 TORCH_DT = {F16: torch.float16, BF16: torch.bfloat16}
 # (block_M, block_N, threads); 256 queries on 256 threads = two 32-query blocks per wave
-TILES = [(128, 64, 256), (256, 64, 512), (128, 128, 256), (256, 64, 256)]
+TILES = [(128, 64, 256), (256, 64, 512), (128, 128, 256), (256, 128, 512), (256, 64, 256)]
 
 
 def dev(u16, dtype):
@@ -79,7 +79,7 @@ def test_explicit_scale():
     assert_close(run(w, Q, K, V, (256, 64, 512), 3, scale=0.3), want, BF16, "scale 0.3")
 
 
-@pytest.mark.parametrize("tile", [(128, 64, 256), (256, 64, 256)], ids=lambda t: "bm%d_bn%d_t%d" % t)
+@pytest.mark.parametrize("tile", [(128, 64, 256), (256, 64, 256), (256, 128, 512)], ids=lambda t: "bm%d_bn%d_t%d" % t)
 @pytest.mark.parametrize("name", ["attn_f16_b4_h32_s4096_d128", "attn_f16_b4_h32_s4096_d128_causal",
                                   "attn_bf16_b2_h32_kv8_s2048_d128_causal"])
 def test_full_size_sampled_rows(name, tile):
