@@ -3,7 +3,7 @@
 A step is one GEMM call, C = A[M,K] . B^T, on inputs already resident in
 HBM.  The headline workload is the 4096^3 fp16 NT GEMM; `value` is its
 throughput in TFLOP/s (2MNK / t) with the fastest configuration (256x256x64
-tile, two stages plus a leading A tile, 4 waves).  The line also carries the
+tile, two stages plus a leading A tile, 8 waves).  The line also carries the
 num_stages sweep of the 128x128x32 tile (the tutorial's default) and of the
 256x256 tiles, the roofline of the kernel (MFMA bound, measured with HIP
 events on the launch stream), and the CPU oracle timed on a bounded row
@@ -294,6 +294,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle", type=int, default=500,
+                    help="back-to-back launches of the timed configuration before its warmup (power settling)")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-attention", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -383,7 +385,12 @@ def main():
     else:
         stages, a_lead = HEADLINE["num_stages"], HEADLINE["a_lead"]
     threads = args.threads if args.threads is not None else HEADLINE["threads"]
-    ms = time_gemm(fn, dA, dB, C, block, stages, threads, steps=args.steps, warmup=args.warmup, a_lead=a_lead)
+    # settle: the power manager needs a few tens of milliseconds of sustained
+    # load before the clock holds steady (from idle the first launches run
+    # boosted, then dip well below the sustained rate), so the timed launches
+    # follow `settle` back-to-back launches whatever ran before them
+    ms = time_gemm(fn, dA, dB, C, block, stages, threads, steps=args.steps, warmup=args.settle + args.warmup,
+                   a_lead=a_lead)
     tflops = flops / ms / 1e9
     _log("headline %s tile %s S=%d%s threads=%d: %.3f ms, %.1f TFLOP/s"
          % (w.name, block, stages, "+A" if a_lead else "", threads, ms, tflops))
@@ -414,16 +421,20 @@ def main():
     try:
         if args.no_context:
             raise RuntimeError("skipped")
-        torch.matmul(dA, dB.t())
+        # the same settle, warmup and launch count as the headline
+        Ct = torch.empty_like(C)
+        for _ in range(args.settle + args.warmup):
+            torch.matmul(dA, dB.t(), out=Ct)
         torch.cuda.synchronize()
         t0 = torch.cuda.Event(enable_timing=True)
         t1 = torch.cuda.Event(enable_timing=True)
         t0.record()
-        for _ in range(20):
-            torch.matmul(dA, dB.t())
+        for _ in range(args.steps):
+            torch.matmul(dA, dB.t(), out=Ct)
         t1.record()
         torch.cuda.synchronize()
-        ref = round(flops / (t0.elapsed_time(t1) / 20) / 1e9, 1)
+        ref = round(flops / (t0.elapsed_time(t1) / args.steps) / 1e9, 1)
+        del Ct
     except Exception as e:  # context only
         _log("torch.matmul context failed: %s" % e)
 
@@ -439,6 +450,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_launches": args.settle,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "strong",
