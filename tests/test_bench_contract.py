@@ -1,0 +1,70 @@
+"""Host-side checks of bench.py's contract (no GPU): the one-GPU refusal, the
+ring-depth notation, the headline configuration's validity and the lookup of
+profiled HBM traffic by kernel-source hash."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+@pytest.mark.parametrize("text,want", [("1", (1, 0)), ("3", (3, 0)), ("2+A", (2, 1)), ("3+A", (3, 1))])
+def test_ring_depth_notation(text, want):
+    assert bench.parse_depth(text) == want
+
+
+def test_headline_configuration_passes_validation():
+    import software_pipelined_tiled_03_amd as pg
+
+    h = bench.HEADLINE
+    bm, bn, bk = h["block"]
+    # pure host validation against the gfx950 budget: no device is touched
+    assert pg.gemm_check(pg.GEMM_NT, 4096, 4096, 4096, pg.GEMM_F16, bm, bn, bk, h["num_stages"], h["threads"],
+                         163840, a_lead=h["a_lead"]) == 0
+
+
+def test_every_sweep_point_is_a_valid_configuration():
+    import software_pipelined_tiled_03_amd as pg
+    from software_pipelined_tiled_03_amd import inputs
+
+    for label, wl, block, threads, depths in bench.SWEEPS:
+        w = inputs.workload(wl)
+        for d in depths:
+            s, lead = bench.parse_depth(d)
+            layout = pg.GEMM_NT if w.layout == "nt" else pg.GEMM_NN
+            st = pg.gemm_check(layout, w.M, w.N, w.K, w.dtype, block[0], block[1], block[2], s, threads, 163840,
+                               a_lead=lead)
+            assert st == 0, (label, d, st)
+
+
+def test_profiled_traffic_is_used_only_for_the_profiled_sources(monkeypatch):
+    h = bench.HEADLINE
+    args = (h["block"], h["num_stages"], h["a_lead"], h["threads"])
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0" * 64)
+    assert bench.measured_traffic(*args) is None
+    # the hash recorded in the headline profile, if one is committed, brings back its figure
+    path = os.path.join(bench.PROFILES, "gemm_nt_f16_4096_256x256x64_s2a_t512.md")
+    if not os.path.exists(path):
+        pytest.skip("no headline profile committed")
+    fields = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip()
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda: fields["source_sha256"])
+    assert bench.measured_traffic(*args) == int(fields["hbm_bytes_per_launch"])
+    # compulsory traffic 2(MK + NK + MN) is a lower bound for what a launch moves
+    assert int(fields["hbm_bytes_per_launch"]) >= 2 * 3 * 4096 * 4096
