@@ -130,6 +130,19 @@ def _device_inputs(w):
     return A, B, dA, dB
 
 
+LDS_PER_CU = 163840
+CUS = 256
+
+
+def shape_ceiling(M, N, K, block):
+    """The most a shape can reach on this tile, in TFLOP/s: the nominal peak
+    times the fraction of compute units its grid can occupy at once and the
+    fraction of the padded tile work that is useful (ragged edges)."""
+    bm, bn, bk = block
+    tm, tn, nk = -(-M // bm), -(-N // bn), -(-K // bk)
+    return PEAK_TFLOPS * min(1.0, tm * tn / CUS) * (M * N * K) / (tm * bm * tn * bn * nk * bk)
+
+
 def time_gemm(fn, dA, dB, C, block, stages, threads, steps, warmup, a_lead=0, relu=False):
     """Average milliseconds per call over `steps` back-to-back launches."""
     import torch
@@ -213,19 +226,32 @@ def attention_sweep(steps=10, warmup=3):
     return out
 
 
-def cpu_baseline(w, A, B, rows):
-    """The CPU oracle (as it stands) on the first `rows` rows of C."""
+def cpu_baseline(w, A, B, rows, gpu_c=None):
+    """The CPU oracle (as it stands) on the first `rows` rows of C.  With
+    `gpu_c` (the headline launch's C as 16-bit encodings) the same rows are
+    also compared with the oracle's: max abs / rel error and the count outside
+    |gpu - oracle| <= 1e-2 + 1e-2 |oracle|."""
+    import numpy as np
+
     from oracle import gemm as og
 
     fn = og.gemm_nt if w.layout == "nt" else og.gemm_nn
     fn(A, B, w.dtype, rows=(0, 1))  # load / warm
     t0 = time.perf_counter()
-    fn(A, B, w.dtype, rows=(0, rows))
+    ref = fn(A, B, w.dtype, rows=(0, rows))
     dt = time.perf_counter() - t0
     flops = 2.0 * rows * w.N * w.K
-    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=og.num_threads(), kind="oracle",
-                sample="rows 0..%d of C (%d x %d x %d, %s), %.1f GFLOP in %.2f s"
-                       % (rows - 1, w.M, w.N, w.K, w.layout.upper(), flops / 1e9, dt))
+    out = dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=og.num_threads(), kind="oracle",
+               sample="rows 0..%d of C (%d x %d x %d, %s), %.1f GFLOP in %.2f s"
+                      % (rows - 1, w.M, w.N, w.K, w.layout.upper(), flops / 1e9, dt))
+    if gpu_c is not None:
+        want = og.decode(ref, w.dtype).astype(np.float64)
+        got = og.decode(gpu_c[:rows], w.dtype).astype(np.float64)
+        err = np.abs(got - want)
+        out["parity"] = dict(rows=rows, elements=int(err.size), max_abs_err=float(err.max()),
+                             max_rel_err=float((err / np.maximum(np.abs(want), 1e-3)).max()),
+                             outside_tolerance=int((err > 1e-2 + 1e-2 * np.abs(want)).sum()))
+    return out
 
 
 # Oracle timing table: (workload, timed runs, also on one thread)
@@ -364,9 +390,12 @@ def main():
             for d in stages:
                 s, lead = parse_depth(d)
                 ms = time_gemm(sfn, sA, sB, sC, block, s, th, steps=30, warmup=5, a_lead=lead)
+                lds = pg.gemm_lds_bytes(block[0], block[1], block[2], s, a_lead=lead)
                 row[d] = dict(tflops=round(sflops / ms / 1e9, 1),
                               pct_peak=round(100 * sflops / ms / 1e9 / PEAK_TFLOPS, 1),
-                              lds_bytes=pg.gemm_lds_bytes(block[0], block[1], block[2], s, a_lead=lead))
+                              pct_shape_ceiling=round(100 * sflops / ms / 1e9 / shape_ceiling(sA.shape[0], sC.shape[1],
+                                                                                               sA.shape[1], block), 1),
+                              lds_bytes=lds, wgs_per_cu_by_lds=LDS_PER_CU // lds, us=round(ms * 1e3, 2))
                 _log("sweep %s S=%s: %.1f TFLOP/s" % (label, d, sflops / ms / 1e9))
             sweep[label] = row
         rej = None
@@ -392,6 +421,9 @@ def main():
     ms = time_gemm(fn, dA, dB, C, block, stages, threads, steps=args.steps, warmup=args.settle + args.warmup,
                    a_lead=a_lead)
     tflops = flops / ms / 1e9
+    # the headline's C (16-bit encodings), for the parity check of the CPU-baseline leg
+    import numpy as np
+    headline_c = None if args.no_cpu_baseline else C.view(torch.int16).cpu().numpy().view(np.uint16)
     _log("headline %s tile %s S=%d%s threads=%d: %.3f ms, %.1f TFLOP/s"
          % (w.name, block, stages, "+A" if a_lead else "", threads, ms, tflops))
 
@@ -440,7 +472,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, A, B, min(args.cpu_rows, w.M))
+        cpu = cpu_baseline(w, A, B, min(args.cpu_rows, w.M), gpu_c=headline_c)
         _log("cpu oracle: %.4f TFLOP/s on %d threads" % (cpu["value"], cpu["cores"]))
 
     out = {
