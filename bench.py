@@ -32,6 +32,7 @@ SWEEPS = [
     ("cfg2_1024_tile128x128x32_t256", "nt_f16_1024", (128, 128, 32), 256, ("1", "2", "3")),
     ("cfg2_1024_tile64x128x64_t256", "nt_f16_1024", (64, 128, 64), 256, ("2", "3", "4")),
     ("cfg5a_ragged_tile128x128x32_t256", "nt_f16_ragged_4000x5000x3000", (128, 128, 32), 256, ("3",)),
+    ("cfg5a_ragged_tile256x256x64_t512", "nt_f16_ragged_4000x5000x3000", (256, 256, 64), 512, ("2", "2+A")),
     ("cfg5b_longk_tile128x128x32_t256", "nt_f16_longk_512x512x65536", (128, 128, 32), 256, ("1", "2", "3", "4", "6")),
     # one GPU's share of 4096^3 over 8 GPUs (512 x 4096 x 4096): 256, 128 or 32 workgroups
     ("shard8_tile64x128x64_t256", "nt_f16_shard8_512x4096x4096", (64, 128, 64), 256, ("2", "3", "4", "6")),
