@@ -161,6 +161,9 @@ int validate(int layout, int64_t M, int64_t N, int64_t K, int dtype, int bm, int
                     (long long)panel);
     if (layout == GEMM_NN && K * N * 2 >= lim)
         return fail(GEMM_ERR_UNSUPPORTED, "B of the NN form must be below 2 GiB");
+    if ((int64_t)bm * N * 2 >= lim)
+        return fail(GEMM_ERR_UNSUPPORTED, "a %lld-byte panel of C rows exceeds the 2 GiB addressable per workgroup",
+                    (long long)bm * N * 2);
     if (inst)
         *inst = in;
     return ok();

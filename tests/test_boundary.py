@@ -164,3 +164,17 @@ def test_no_device_reported_as_hip_error():
     assert pg.gemm_nt_raw(None, None, None, -1, 4, 8, F16, 128, 128, 32, 2, 0, 256, None) == pg.GEMM_ERR_ARG
     assert pg.gemm_nt_raw(16, 16, 16, 4, 4, 8, F16, 128, 128, 32, 2, 0, 256, None) == pg.GEMM_ERR_HIP
     assert pg.gemm_nt_raw(16, 16, 16, 4, 4, 8, F16, 128, 128, 32, 1, 1, 256, None) == pg.GEMM_ERR_ARG
+
+
+def test_size_limits_of_the_32_bit_offsets():
+    # a workgroup addresses its A and B panels and its rows of C through buffer
+    # resources with 32-bit offsets below 2 GiB
+    lim = 1 << 31
+    assert check(K=lim // (2 * 128) - 8) == pg.GEMM_OK
+    assert check(K=lim // (2 * 128)) == pg.GEMM_ERR_UNSUPPORTED
+    assert "operand panel" in pg.last_error()
+    assert check(N=lim // (2 * 128) - 8, K=64) == pg.GEMM_OK
+    assert check(N=lim // (2 * 128), K=64) == pg.GEMM_ERR_UNSUPPORTED
+    assert "panel of C rows" in pg.last_error()
+    assert check(N=lim // (2 * 256), K=64, bm=256, bn=256, bk=64, s=2, th=512) == pg.GEMM_ERR_UNSUPPORTED
+    assert check(M=lim, K=64) == pg.GEMM_ERR_UNSUPPORTED
