@@ -313,6 +313,13 @@ PG_HD constexpr int spread_part(int kk, int k0, int k1, int n)
 {
     return kk <= k0 ? 0 : (kk >= k1 ? n : (kk - k0) * n / (k1 - k0));
 }
+// Early B (lead rings with S = 2, on the tiles that select it): iteration j
+// issues the B copies of tile j+S right after its barrier, into the slot tile
+// j has just freed, instead of over the first half of iteration j+1's k-steps.
+// The copies go out in the same order (A(t), B(t), A(t+1), ...) and every
+// wait allows the same count; only B's copies leave earlier, which shortens
+// the exposed copy latency when A and B come from HBM.
+PG_HD constexpr bool ring_early_b(int S, int lead, bool wanted) { return wanted && lead == 1 && S == 2; }
 PG_HD constexpr int copy_a_before(int kk, int ks, int la, int lb, int lead)
 {
     return lead ? spread_part(kk, ks / 2, ks, la)

@@ -354,8 +354,9 @@ void check_cbuf(int G)
 // refilled only after its tile was read, that every wait leaves exactly the
 // copies issued after the awaited tile in flight, that each tile is read from
 // the slots its copies went to, and the 63-copy vmcnt bound.
-void check_ring_case(int S, int lead, int la, int lb, int ks, int nk)
+void check_ring_case(int S, int lead, int la, int lb, int ks, int nk, bool early_wanted)
 {
+    const bool early = ring_early_b(S, lead, early_wanted);
     const int SA = S + lead;
     struct Slot {
         int tile = -1;
@@ -411,6 +412,8 @@ void check_ring_case(int S, int lead, int la, int lb, int ks, int nk)
     if (lead)
         issue_a(S - 1, 0, la);
     wait_for(0, ring_wait_first(S, lead, la, lb));
+    if (early)  // after the first barrier: the B copies iteration 0 would issue
+        issue_b(ring_issue_tile_b(0, S, lead), 0, lb);
     for (int j = 0; j < nk; ++j) {
         const int ta = ring_issue_tile_a(j, S, lead), tb = ring_issue_tile_b(j, S, lead);
         for (int kk = 0; kk < ks; ++kk) {
@@ -419,7 +422,8 @@ void check_ring_case(int S, int lead, int la, int lb, int ks, int nk)
                 const int b0 = copy_b_before(kk, ks, la, lb, lead), b1 = copy_b_before(kk + 1, ks, la, lb, lead);
                 CHECK(a0 <= a1 && b0 <= b1, "plan not monotone");
                 if (lead) {
-                    issue_b(tb, b0, b1);
+                    if (!early)
+                        issue_b(tb, b0, b1);
                     issue_a(ta, a0, a1);
                 } else {
                     issue_a(ta, a0, a1);
@@ -438,6 +442,8 @@ void check_ring_case(int S, int lead, int la, int lb, int ks, int nk)
                   "plan does not cover the tile");
         wait_for(j + 1, ring_wait_steady(S, lead, la, lb));
         // barrier
+        if (early)  // B of the tile iteration j+1 would issue, into tile j's freed slot
+            issue_b(tb + 1, 0, lb);
         if (!spread) {
             CHECK(ta == tb && ring_slot(ta, SA) == ring_slot(j, SA), "burst refills the freed slots");
             issue_a(ta, 0, la);
@@ -456,7 +462,8 @@ void check_ring()
             for (auto &l : loads)
                 for (int ks : {1, 2, 4})  // k-steps per tile: BK / 16 (32x32x16) or BK / 32 (16x16x32)
                     for (int nk = 0; nk <= 24; ++nk)
-                        check_ring_case(S, lead, l[0], l[1], ks, nk);
+                        for (bool early : {false, true})
+                            check_ring_case(S, lead, l[0], l[1], ks, nk, early);
     for (int n = 1; n <= 32; ++n)
         CHECK((ring_max_stages(n) - 1) * n <= 63 && ring_max_stages(n) * n > 63, "ring_max_stages(%d)", n);
     // the ring depths the kernel builds: B ring S, A ring S + lead
