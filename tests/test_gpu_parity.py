@@ -187,7 +187,8 @@ def test_one_gpu_share_512x4096x4096(oracle_gemm):
 # Every built tile, both layouts and dtypes, on a shape ragged in M, N and K
 
 TILES = [(64, 128, 64, 256), (128, 128, 32, 128), (128, 128, 32, 256), (128, 128, 32, 512), (128, 128, 64, 256),
-         (128, 256, 32, 256), (128, 256, 64, 256), (256, 128, 32, 256), (256, 128, 64, 256),
+         (128, 256, 32, 256), (128, 256, 64, 256), (128, 256, 64, 512), (256, 128, 32, 256), (256, 128, 32, 512),
+         (256, 128, 64, 256),
          (256, 256, 32, 256), (256, 256, 32, 512), (256, 256, 64, 256), (256, 256, 64, 512)]
 
 
