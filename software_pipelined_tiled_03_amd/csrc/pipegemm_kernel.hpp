@@ -517,13 +517,16 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
             if (i >= first && i < last)
                 acc[i / FN][i % FN] = MM::run(fb[buf][i % FN], fa[buf][i / FN], acc[i / FN][i % FN]);
     };
-    // One operand read j (A fragments first, then B) of k-step kk into buffer buf.
+    // One operand fragment j (A fragments first, then B; an NN B fragment is
+    // two transposed reads) of k-step kk into buffer buf.
     auto read_one = [&](const char *as_, const char *bs_, auto kk_c, int buf, auto j_c) __attribute__((always_inline)) {
         constexpr int kk = decltype(kk_c)::value, j = decltype(j_c)::value;
         if constexpr (j < FM)
             fa[buf][j] = *(const frag *)(as_ + a_rd[kk] + j * MF * BK * 2);
-        else
+        else if constexpr (!NN)
             fb[buf][j - FM] = *(const frag *)(bs_ + b_rd[kk] + (j - FM) * MF * BK * 2);
+        else
+            fb[buf][j - FM] = load_b_nn<T, Cfg>(bs_, kk, wn * Cfg::TN + (j - FM) * MF, lane);
     };
     // MFMAs [M0, M0 + NM) of buffer buf in an explicit issue order: after the
     // i-th MFMA the i-th of NR operand reads (rd), and the NC copies (cp)
@@ -573,7 +576,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
         constexpr int SA = S + LEAD;
         // early B (measured on the 8-wave 256 x 256 NT tile: same warm time,
         // 4-6 % less with the caches scrubbed at 4096^3)
-        constexpr bool kEarlyB = ring_early_b(S, LEAD, kPrio && !NN);
+        constexpr bool kEarlyB = ring_early_b(S, LEAD, kPrio);
         char *const ring_a = smem;
         char *const ring_b = smem + SA * Cfg::A_BYTES;
         if constexpr (S == 1) {
@@ -680,7 +683,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
                         issue_b(tb + 1, (char *)bs, c, c + 1);
                     };
                     stretch(std::integral_constant<int, kMfma - kMfma / 2>(), std::integral_constant<int, kMfma / 2>(), last,
-                            std::integral_constant<int, kReads>(), rd, std::integral_constant<int, kLB>(), cp);
+                            std::integral_constant<int, FM + FN>(), rd, std::integral_constant<int, kLB>(), cp);
                     set_prio(std::integral_constant<int, 0>());
                     ra = na;
                     rb = nb;
