@@ -67,7 +67,10 @@ enum gemm_status {
     GEMM_ERR_ARG = 1,         /* negative size, null pointer, unknown dtype/layout, bad block/stage/thread value */
     GEMM_ERR_LDS_BUDGET = 2,  /* num_stages x (block_M + block_N) x block_K x 2 bytes (+ block_M x block_K x 2
                                  with a_lead) exceeds the LDS limit */
-    GEMM_ERR_UNSUPPORTED = 3, /* no kernel is built for this (dtype, layout, tile, threads) or size limits exceeded */
+    GEMM_ERR_UNSUPPORTED = 3, /* no kernel is built for this (dtype, layout, tile, threads), or a size limit of
+                                 the kernels' 32-bit buffer offsets is exceeded: M, N, K below 2^31, and below
+                                 2 GiB each of max(block_M, block_N) x K x 2 (a workgroup's A or B panel),
+                                 block_M x N x 2 (its rows of C) and, for NN, K x N x 2 (B) */
     GEMM_ERR_ALIGN = 4,       /* K (and N for NN) not a multiple of 8, or misaligned pointers */
     GEMM_ERR_HIP = 5          /* a HIP runtime call failed (no device, launch failure) */
 };
