@@ -51,7 +51,7 @@ SWEEPS = [
     ("nn_bf16_tile128x256x64_t256", "nn_bf16_4096", (128, 256, 64), 256, ("1", "2", "3")),
     ("nn_bf16_tile256x128x32_t256", "nn_bf16_4096", (256, 128, 32), 256, ("1", "2", "3", "4", "6")),
     # the same two tiles on 8 waves (16x16x32 MFMAs, two waves per SIMD)
-    ("nn_bf16_tile128x256x64_t512", "nn_bf16_4096", (128, 256, 64), 512, ("1", "2", "3")),
+    ("nn_bf16_tile128x256x64_t512", "nn_bf16_4096", (128, 256, 64), 512, ("1", "2", "3", "3+A")),
     ("nn_bf16_tile256x128x32_t512", "nn_bf16_4096", (256, 128, 32), 512, ("1", "2", "3", "4", "6")),
     ("nn_bf16_tile256x256x64_t256", "nn_bf16_4096", (256, 256, 64), 256, ("2", "2+A")),
     ("nn_bf16_tile256x256x64_t512", "nn_bf16_4096", (256, 256, 64), 512, ("2", "2+A")),
