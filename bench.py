@@ -5,9 +5,12 @@ HBM.  The headline workload is the 4096^3 fp16 NT GEMM; `value` is its
 throughput in TFLOP/s (2MNK / t) with the fastest configuration (256x256x64
 tile, two stages plus a leading A tile, 8 waves).  The line also carries the
 num_stages sweep of the 128x128x32 tile (the tutorial's default) and of the
-256x256 tiles, the roofline of the kernel (MFMA bound, measured with HIP
-events on the launch stream), and the CPU oracle timed on a bounded row
-sample of the same GEMM.
+256x256 tiles (each point timed by the library's own launch loop, with the
+clock, phase times and cycles per K tile of one clock-stamped launch), the
+roofline of the kernel (MFMA bound, measured with HIP events on the launch
+stream), the shader clock the headline ran at with its MFMA utilisation at
+that clock, and the CPU oracle timed on a bounded row sample of the same GEMM
+together with the element-wise parity of the headline's C.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-cpu-baseline]
 """
@@ -34,6 +37,9 @@ SWEEPS = [
     ("cfg5a_ragged_tile128x128x32_t256", "nt_f16_ragged_4000x5000x3000", (128, 128, 32), 256, ("3",)),
     ("cfg5a_ragged_tile256x256x64_t512", "nt_f16_ragged_4000x5000x3000", (256, 256, 64), 512, ("2", "2+A")),
     ("cfg5b_longk_tile128x128x32_t256", "nt_f16_longk_512x512x65536", (128, 128, 32), 256, ("1", "2", "3", "4", "6")),
+    # the same 16 workgroups with 8 waves each (two per SIMD), at block_K 32 and 64
+    ("cfg5b_longk_tile128x128x32_t512", "nt_f16_longk_512x512x65536", (128, 128, 32), 512, ("1", "2", "3", "4", "6")),
+    ("cfg5b_longk_tile128x128x64_t512", "nt_f16_longk_512x512x65536", (128, 128, 64), 512, ("1", "2", "3", "4", "5")),
     # one GPU's share of 4096^3 over 8 GPUs (512 x 4096 x 4096): 256, 128 or 32 workgroups
     ("shard8_tile64x128x64_t256", "nt_f16_shard8_512x4096x4096", (64, 128, 64), 256, ("2", "3", "4", "6")),
     ("shard8_tile128x128x64_t256", "nt_f16_shard8_512x4096x4096", (128, 128, 64), 256, ("2", "3", "4")),
@@ -140,11 +146,47 @@ CUS = 256
 
 def shape_ceiling(M, N, K, block):
     """The most a shape can reach on this tile, in TFLOP/s: the nominal peak
-    times the fraction of compute units its grid can occupy at once and the
-    fraction of the padded tile work that is useful (ragged edges)."""
+    times the fraction of compute-unit time its grid can fill (the tiles go
+    out in ceil(tiles / 256) rounds over the 256 compute units; a tile keeps
+    at most one compute unit busy) and the fraction of the padded tile work
+    that is useful (ragged edges)."""
     bm, bn, bk = block
     tm, tn, nk = -(-M // bm), -(-N // bn), -(-K // bk)
-    return PEAK_TFLOPS * min(1.0, tm * tn / CUS) * (M * N * K) / (tm * bm * tn * bn * nk * bk)
+    tiles = tm * tn
+    rounds = -(-tiles // CUS)
+    return PEAK_TFLOPS * tiles / (rounds * CUS) * (M * N * K) / (tm * bm * tn * bn * nk * bk)
+
+
+def stamp_summary(stamps, nk, flops=None, ms=None):
+    """Reduce gemm_stamped's six counters per workgroup (cycles at start,
+    after the prologue, after the K loop and at the end; 100 MHz real time at
+    start and end): the shader clock (mean over workgroups, and per XCD =
+    workgroup id mod 8), the median prologue, K-loop and epilogue times, the
+    K-loop cycles per K tile (median over workgroups), the workgroups resident
+    per compute unit on average (summed workgroup time over the span times
+    256), and with `flops` and `ms` (the event time per launch) the MFMA
+    utilisation at the measured clock."""
+    import numpy as np
+
+    s = stamps.view(-1, 6).cpu().numpy().astype(np.float64)
+    cyc, rt = s[:, 3] - s[:, 0], s[:, 5] - s[:, 4]
+    ok = rt > 0
+    clk = np.where(ok, cyc / np.where(ok, rt, 1) * 0.1, np.nan)  # GHz
+    clock = float(np.nanmean(clk))
+    xcd = np.arange(len(s)) % 8
+    per_xcd = [round(float(np.nanmean(clk[xcd == x])), 3) if (xcd == x).any() else None for x in range(8)]
+    to_us = lambda c: float(np.median(c / clk)) / 1e3
+    span_us = float(s[:, 5].max() - s[:, 4].min()) / 100.0
+    out = dict(clock_ghz=round(clock, 3), clock_ghz_per_xcd=per_xcd,
+               clock_ghz_min_xcd=round(float(np.nanmin([c for c in per_xcd if c is not None])), 3),
+               prologue_us=round(to_us(s[:, 1] - s[:, 0]), 3), loop_us=round(to_us(s[:, 2] - s[:, 1]), 3),
+               epilogue_us=round(to_us(s[:, 3] - s[:, 2]), 3),
+               loop_cycles_per_k_tile=round(float(np.median(s[:, 2] - s[:, 1])) / max(nk, 1), 1),
+               wg_span_us=round(span_us, 3),
+               wgs_resident_per_cu=round(float(rt.sum()) / 100.0 / (span_us * CUS), 2) if span_us > 0 else None)
+    if flops is not None and ms:
+        out["mfma_util_at_clock"] = round(flops / (ms * 1e-3) / (CUS * 4096 * clock * 1e9), 4)
+    return out
 
 
 def time_gemm(fn, dA, dB, C, block, stages, threads, steps, warmup, a_lead=0, relu=False):
@@ -252,9 +294,11 @@ def cpu_baseline(w, A, B, rows, gpu_c=None):
         want = og.decode(ref, w.dtype).astype(np.float64)
         got = og.decode(gpu_c[:rows], w.dtype).astype(np.float64)
         err = np.abs(got - want)
-        out["parity"] = dict(rows=rows, elements=int(err.size), max_abs_err=float(err.max()),
-                             max_rel_err=float((err / np.maximum(np.abs(want), 1e-3)).max()),
-                             outside_tolerance=int((err > 1e-2 + 1e-2 * np.abs(want)).sum()))
+        out["parity_rows"] = rows
+        out["parity_elements"] = int(err.size)
+        out["parity_outside_tolerance"] = int((err > 1e-2 + 1e-2 * np.abs(want)).sum())
+        out["parity_max_abs_err"] = float(err.max())
+        out["parity_max_rel_err"] = float((err / np.maximum(np.abs(want), 1e-3)).max())
     return out
 
 
@@ -330,7 +374,7 @@ def main():
     ap.add_argument("--no-attention", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096)
-    ap.add_argument("--no-context", action="store_true", help="skip the torch.matmul context timing")
+    ap.add_argument("--no-clock", action="store_true", help="skip the clock-stamped launches after the headline")
     ap.add_argument("--workload", default=HEADLINE["workload"], help="one of inputs.WORKLOADS")
     ap.add_argument("--block", default=None, help="tile as BMxBNxBK (default: the headline tile)")
     ap.add_argument("--stages", default=None, help="ring depth, e.g. 3 or 2+A (num_stages 2 with a_lead)")
@@ -389,18 +433,33 @@ def main():
                 operands[wl] = (sA, sB, torch.empty((ws.M, ws.N), dtype=sA.dtype, device="cuda"),
                                 pg.gemm_nt if ws.layout == "nt" else pg.gemm_nn)
             sA, sB, sC, sfn = operands[wl]
-            sflops = 2.0 * sA.shape[0] * sC.shape[1] * sA.shape[1]
+            lay = "nt" if sfn is pg.gemm_nt else "nn"
+            sM, sK, sN = sA.shape[0], sA.shape[1], sC.shape[1]
+            sflops = 2.0 * sM * sN * sK
             row = {}
             for d in stages:
                 s, lead = parse_depth(d)
-                ms = time_gemm(sfn, sA, sB, sC, block, s, th, steps=30, warmup=5, a_lead=lead)
+                cfg = dict(block_M=block[0], block_N=block[1], block_K=block[2], num_stages=s, a_lead=lead,
+                           threads=th)
+                # the library's own timing loop (no per-call host cost in the figure)
+                ms = pg.tuning.time_config(sA, sB, cfg, layout=lay, warmup=5, reps=30, out=sC)
+                # one more launch with clock stamps: clock, phases, cycles per K tile
+                _, stamps = pg.gemm_stamped(pg.GEMM_NT if lay == "nt" else pg.GEMM_NN, sA, sB, out=sC, block=block,
+                                            num_stages=s, threads=th, a_lead=lead)
+                st = stamp_summary(stamps, -(-sK // block[2]), sflops, ms)
                 lds = pg.gemm_lds_bytes(block[0], block[1], block[2], s, a_lead=lead)
                 row[d] = dict(tflops=round(sflops / ms / 1e9, 1),
                               pct_peak=round(100 * sflops / ms / 1e9 / PEAK_TFLOPS, 1),
-                              pct_shape_ceiling=round(100 * sflops / ms / 1e9 / shape_ceiling(sA.shape[0], sC.shape[1],
-                                                                                               sA.shape[1], block), 1),
-                              lds_bytes=lds, wgs_per_cu_by_lds=LDS_PER_CU // lds, us=round(ms * 1e3, 2))
-                _log("sweep %s S=%s: %.1f TFLOP/s" % (label, d, sflops / ms / 1e9))
+                              pct_shape_ceiling=round(100 * sflops / ms / 1e9 / shape_ceiling(sM, sN, sK, block), 1),
+                              lds_bytes=lds, wgs_per_cu_by_lds=LDS_PER_CU // lds, us=round(ms * 1e3, 2),
+                              clock_ghz=st["clock_ghz"], mfma_util_at_clock=st.get("mfma_util_at_clock"),
+                              loop_cycles_per_k_tile=st["loop_cycles_per_k_tile"],
+                              wgs_resident_per_cu=st["wgs_resident_per_cu"],
+                              copy_bytes_per_cycle_per_wg=round((block[0] + block[1]) * block[2] * 2
+                                                                / st["loop_cycles_per_k_tile"], 2),
+                              prologue_us=st["prologue_us"], epilogue_us=st["epilogue_us"])
+                _log("sweep %s S=%s: %.1f TFLOP/s at %.2f GHz, %.0f cycles per K tile"
+                     % (label, d, sflops / ms / 1e9, st["clock_ghz"], st["loop_cycles_per_k_tile"]))
             sweep[label] = row
         rej = None
         nA, nB, nC, nfn = operands.get("nn_bf16_4096", (None, None, None, None))
@@ -431,6 +490,32 @@ def main():
     _log("headline %s tile %s S=%d%s threads=%d: %.3f ms, %.1f TFLOP/s"
          % (w.name, block, stages, "+A" if a_lead else "", threads, ms, tflops))
 
+    # the same configuration, right after the timed launches, with clock
+    # stamps: the shader clock the chip actually ran at (it is power-limited
+    # with random operands), per XCD, and the MFMA utilisation at that clock
+    clock = None
+    if not args.no_clock:
+        layout_code = pg.GEMM_NT if w.layout == "nt" else pg.GEMM_NN
+        grid = -(-w.M // block[0]) * -(-w.N // block[1])
+        stamps = torch.zeros(6 * grid, dtype=torch.int64, device="cuda")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        e0.record()
+        for _ in range(reps):
+            pg.gemm_stamped(layout_code, dA, dB, out=C, block=block, num_stages=stages, threads=threads,
+                            a_lead=a_lead, stamps=stamps)
+        e1.record()
+        torch.cuda.synchronize()
+        sms = e0.elapsed_time(e1) / reps
+        # utilisation against the timed launches' own time, at the clock the
+        # launches right after them ran at
+        clock = stamp_summary(stamps, -(-w.K // block[2]), flops, ms)
+        clock["launches"] = reps
+        clock["ms_per_launch"] = round(sms, 5)
+        _log("clock %.3f GHz (XCDs %s), MFMA utilisation at that clock %.3f; prologue %.2f us, loop %.2f us, "
+             "epilogue %.2f us" % (clock["clock_ghz"], clock["clock_ghz_per_xcd"], clock["mfma_util_at_clock"],
+                                  clock["prologue_us"], clock["loop_us"], clock["epilogue_us"]))
+
     # per-launch distribution of the same configuration, warm and with the
     # caches scrubbed (512 MiB written between launches: twice the MALL)
     per_launch = None
@@ -451,28 +536,6 @@ def main():
     relu_ms = time_gemm(fn, dA, dB, C, block, stages, threads, steps=max(10, args.steps // 2), warmup=args.warmup,
                         a_lead=a_lead, relu=True)
     _log("headline with fused ReLU: %.3f ms, %.1f TFLOP/s" % (relu_ms, flops / relu_ms / 1e9))
-
-    # context: the vendor library on the same operands
-    ref = None
-    try:
-        if args.no_context:
-            raise RuntimeError("skipped")
-        # the same settle, warmup and launch count as the headline
-        Ct = torch.empty_like(C)
-        for _ in range(args.settle + args.warmup):
-            torch.matmul(dA, dB.t(), out=Ct)
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(args.steps):
-            torch.matmul(dA, dB.t(), out=Ct)
-        t1.record()
-        torch.cuda.synchronize()
-        ref = round(flops / (t0.elapsed_time(t1) / args.steps) / 1e9, 1)
-        del Ct
-    except Exception as e:  # context only
-        _log("torch.matmul context failed: %s" % e)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -495,7 +558,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "GEMM %s %dx%dx%d %s, fp32 accumulate" % (
                        w.layout.upper(), w.M, w.N, w.K, "fp16 uniform[-1,1]" if w.dtype == inputs.F16 else "bf16 normal(0,1)"),
-                   "M": w.M, "N": w.N, "K": w.K, "layout": w.layout.upper(), "block": list(block),
+                   "M": w.M, "N": w.N, "K": w.K, "layout": w.layout.upper(), "block": "%dx%dx%d" % tuple(block),
                    "num_stages": stages, "a_lead": a_lead, "threads": threads},
         "pct_peak": round(100 * tflops / PEAK_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_TFLOPS, "unit": "TFLOP/s",
@@ -505,8 +568,8 @@ def main():
         "per_num_stages": sweep,
         "fused_relu": {"tflops": round(flops / relu_ms / 1e9, 2), "ms_per_step": round(relu_ms, 5)},
         "per_launch": per_launch,
+        "clock": clock,
         "attention": attn,
-        "context_torch_matmul_tflops": ref,
     }
     print(json.dumps(out), flush=True)
     return 0

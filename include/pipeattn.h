@@ -37,7 +37,9 @@ extern "C" {
  *   dtype      GEMM_F16 or GEMM_BF16 (pipegemm.h); fp32 scores, softmax and
  *              accumulation; P is rounded to dtype for the second product
  *   is_causal  1: query i sees keys j <= i (needs seq_q == seq_kv)
- *   scale      softmax scale; 0 selects 1 / sqrt(dim)
+ *   scale      softmax scale: 0 selects 1 / sqrt(dim); otherwise it must be
+ *              positive and finite (a negative, infinite or NaN scale is an
+ *              argument error, GEMM_ERR_ARG, reported before anything else)
  *   block_M    queries per workgroup, 32 or 64 per wave (threads = 2 x block_M
  *              or block_M); built: (block_M, block_N, threads) = (128, 64, 256),
  *              (256, 64, 512), (128, 128, 256), (256, 128, 512), (256, 64, 256)

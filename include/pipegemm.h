@@ -130,6 +130,36 @@ int gemm_nn_relu(const void *A, const void *B, void *C, int64_t M, int64_t N, in
                  int block_M, int block_N, int block_K, int num_stages, int a_lead, int threads, void *hip_stream);
 
 /*
+ * gemm_stamped: gemm_nt (layout GEMM_NT) or gemm_nn (GEMM_NN) that also
+ * records, per workgroup, when its phases ran, so the stage-count knee can be
+ * read off measured cycles per K tile: the prologue, steady state and
+ * epilogue of chapter 11, section 4.3, and the copy/compute period of
+ * sections 1.2-1.3 and 2.2.
+ *
+ * Workgroup w (its dispatch index, 0 .. ceil(M/block_M) ceil(N/block_N) - 1;
+ * it runs on XCD w mod 8) writes six counters to stamps[6w .. 6w+5]:
+ *   [0] shader-clock cycle counter (s_memtime) at its start,
+ *   [1] the same once its first K tile has landed (after the prologue),
+ *   [2] the same after its K loop,
+ *   [3] the same at its end (after it issued its stores of C),
+ *   [4] the constant 100 MHz real-time counter (s_memrealtime) at its start,
+ *   [5] the same at its end.
+ * The shader clock of the run is (stamps[3] - stamps[0]) / (stamps[5] -
+ * stamps[4]) x 100 MHz.  The values of different XCDs' cycle counters are
+ * not comparable with each other; differences within one workgroup are.
+ *
+ * stamps: device pointer, 8-byte aligned, to at least 6 x grid uint64 values,
+ * owned by the caller; the kernel only writes it (no count is checked).  All
+ * other arguments, the validation and the errors are those of gemm_nt /
+ * gemm_nn; a null or misaligned stamps pointer is an argument error
+ * (GEMM_ERR_ARG).
+ * The computation and C are the same as without stamps.
+ */
+int gemm_stamped(int layout, const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype,
+                 int block_M, int block_N, int block_K, int num_stages, int a_lead, int threads, void *hip_stream,
+                 uint64_t *stamps);
+
+/*
  * gemm_lds_bytes: LDS the pipeline of one workgroup needs,
  *   max(num_stages, 1) x (block_M x block_K + block_K x block_N) x 2 bytes,
  *   plus block_M x block_K x 2 bytes when a_lead is 1.

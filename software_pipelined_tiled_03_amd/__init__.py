@@ -9,14 +9,15 @@ from .binding import (GEMM_BF16, GEMM_F16, GEMM_NN, GEMM_NT, AlignmentError, Gem
                       attention, attn_check, attn_fwd_raw, attn_lds_bytes,
                       GemmHipError, LdsBudgetError, UnsupportedConfigError, gemm_check, gemm_lds_budget,
                       gemm_lds_bytes, gemm_nn, gemm_nn_raw, gemm_nn_relu_raw, gemm_nt, gemm_nt_raw, gemm_nt_relu_raw,
-                      last_error, load)
+                      gemm_stamped, gemm_stamped_raw, last_error, load)
+from . import tuning
 from .tuning import (RANKED_OUT, TuneResult, TuningSpaceError, built_configs, default_config, matmul, model_costs, plan,
                      prune, rank, tune)
 
 __all__ = ["GEMM_BF16", "GEMM_F16", "GEMM_NN", "GEMM_NT", "AlignmentError", "GemmArgumentError", "GemmError",
            "GemmHipError", "LdsBudgetError", "UnsupportedConfigError", "gemm_check", "gemm_lds_budget",
            "gemm_lds_bytes", "gemm_nn", "gemm_nn_raw", "gemm_nn_relu_raw", "gemm_nt", "gemm_nt_raw",
-           "gemm_nt_relu_raw", "last_error", "load",
+           "gemm_nt_relu_raw", "gemm_stamped", "gemm_stamped_raw", "last_error", "load",
            "attention", "attn_check", "attn_fwd_raw", "attn_lds_bytes",
            "RANKED_OUT", "TuneResult", "TuningSpaceError", "built_configs", "default_config", "matmul",
            "model_costs", "plan", "prune", "rank", "tune"]

@@ -76,6 +76,8 @@ def load():
         f = getattr(lib, name)
         f.argtypes = [vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, i32, vp]
         f.restype = i32
+    lib.gemm_stamped.argtypes = [i32, vp, vp, vp, i64, i64, i64, i32, i32, i32, i32, i32, i32, i32, vp, vp]
+    lib.gemm_stamped.restype = i32
     lib.gemm_lds_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.gemm_lds_bytes.restype = i64
     lib.gemm_lds_budget.argtypes = []
@@ -123,6 +125,13 @@ def gemm_nn_relu_raw(A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_sta
                                hip_stream)
 
 
+def gemm_stamped_raw(layout, A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, a_lead, threads,
+                     hip_stream, stamps):
+    """gemm_stamped on raw device addresses; returns the status code."""
+    return load().gemm_stamped(layout, A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, a_lead,
+                               threads, hip_stream, stamps)
+
+
 def gemm_lds_bytes(block_M, block_N, block_K, num_stages, dtype=GEMM_F16, a_lead=0) -> int:
     return int(load().gemm_lds_bytes(block_M, block_N, block_K, num_stages, a_lead, dtype))
 
@@ -151,7 +160,7 @@ def _dtype_code(t):
     raise GemmArgumentError(GEMM_ERR_ARG, "dtype must be float16 or bfloat16, got %s" % t.dtype)
 
 
-def _gemm(layout, A, B, out, block, num_stages, threads, stream, a_lead, relu=False):
+def _gemm(layout, A, B, out, block, num_stages, threads, stream, a_lead, relu=False, stamps=None):
     import torch
     if A.dim() != 2 or B.dim() != 2:
         raise GemmArgumentError(GEMM_ERR_ARG, "A and B must be 2-D")
@@ -183,10 +192,32 @@ def _gemm(layout, A, B, out, block, num_stages, threads, stream, a_lead, relu=Fa
     else:
         fn = lib.gemm_nt if layout == GEMM_NT else lib.gemm_nn
     with torch.cuda.device(A.device):
-        st = fn(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K, _dtype_code(A), bm, bn, bk, num_stages,
-                int(a_lead), threads, stream)
+        if stamps is not None:
+            st = lib.gemm_stamped(layout, A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K, _dtype_code(A), bm, bn,
+                                  bk, num_stages, int(a_lead), threads, stream, stamps.data_ptr())
+        else:
+            st = fn(A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K, _dtype_code(A), bm, bn, bk, num_stages,
+                    int(a_lead), threads, stream)
     _raise_for(st)
     return out
+
+
+def gemm_stamped(layout, A, B, out=None, block=(128, 128, 32), num_stages=3, threads=256, stream=None, a_lead=0,
+                 stamps=None):
+    """gemm_nt / gemm_nn (layout GEMM_NT / GEMM_NN) that also writes six clock
+    counters per workgroup into `stamps` (an int64 device tensor of at least
+    6 x grid elements; allocated when None).  Returns (C, stamps)."""
+    import torch
+    M, K = A.shape
+    N = B.shape[0] if layout == GEMM_NT else B.shape[1]
+    grid = -(-M // block[0]) * -(-N // block[1])
+    if stamps is None:
+        stamps = torch.zeros(6 * grid, dtype=torch.int64, device=A.device)
+    elif (stamps.dtype != torch.int64 or not stamps.is_contiguous() or stamps.numel() < 6 * grid
+          or stamps.device != A.device):
+        raise GemmArgumentError(GEMM_ERR_ARG, "stamps must be a contiguous int64 device tensor of >= 6 x grid values")
+    out = _gemm(layout, A, B, out, block, num_stages, threads, stream, a_lead, stamps=stamps)
+    return out, stamps
 
 
 def gemm_nt(A, B, out=None, block=(128, 128, 32), num_stages=3, threads=256, stream=None, a_lead=0, relu=False):

@@ -196,7 +196,8 @@ int device_budget(int64_t *out)
 }
 
 int run(int layout, const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype, int bm,
-        int bn, int bk, int stages, int lead, int threads, void *stream, int relu = 0)
+        int bn, int bk, int stages, int lead, int threads, void *stream, int relu = 0,
+        unsigned long long *stamps = nullptr)
 {
     const void *ptrs[3] = {A, B, C};
     // Argument errors are reported as such even when no device can be queried:
@@ -230,6 +231,7 @@ int run(int layout, const void *A, const void *B, void *C, int64_t M, int64_t N,
     a.group_m = a.tiles_m < 4 ? a.tiles_m : 4;
     a.c_vec = (N % 8) == 0 && ((uintptr_t)C & 15) == 0;
     a.relu = relu;
+    a.stamps = stamps;
     const int64_t grid = (int64_t)a.tiles_m * a.tiles_n;
     if (grid >= (1LL << 31))
         return fail(GEMM_ERR_UNSUPPORTED, "too many tiles");
@@ -420,6 +422,11 @@ int attn_fwd(const void *Q, const void *K, const void *V, void *O, int64_t batch
              int block_N, int num_stages, int threads, void *hip_stream)
 {
     using namespace pipegemm;
+    // (1) arguments: the scale is 0 (the default 1/sqrt(dim)) or a positive
+    // finite number; a negative one would turn the -inf of masked scores
+    // into +inf
+    if (!(scale >= 0.0f) || !std::isfinite(scale))
+        return fail(GEMM_ERR_ARG, "scale must be 0 (1/sqrt(dim)) or positive and finite (got %g)", (double)scale);
     const void *ptrs[4] = {Q, K, V, O};
     int st = attn_validate(batch, heads, kv_heads, seq_q, seq_kv, dim, dtype, is_causal, block_M, block_N,
                            num_stages, threads, 1LL << 40, ptrs, nullptr);
@@ -446,7 +453,7 @@ int attn_fwd(const void *Q, const void *K, const void *V, void *O, int64_t batch
     a.Skv = (int)seq_kv;
     a.groups = (int)(heads / kv_heads);
     a.causal = is_causal;
-    const float sc = scale > 0.0f ? scale : 1.0f / sqrtf((float)dim);
+    const float sc = scale == 0.0f ? 1.0f / sqrtf((float)dim) : scale;
     a.scale_log2 = sc * 1.4426950408889634f;  // log2(e)
     a.stages = num_stages < 1 ? 1 : num_stages;
     a.nq = (int)((seq_q + block_M - 1) / block_M);
@@ -643,6 +650,18 @@ int gemm_nn_relu(const void *A, const void *B, void *C, int64_t M, int64_t N, in
 {
     return pipegemm::run(GEMM_NN, A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, a_lead, threads,
                          hip_stream, 1);
+}
+
+int gemm_stamped(int layout, const void *A, const void *B, void *C, int64_t M, int64_t N, int64_t K, int dtype,
+                 int block_M, int block_N, int block_K, int num_stages, int a_lead, int threads, void *hip_stream,
+                 uint64_t *stamps)
+{
+    // an argument error, so it is reported before the budget as the
+    // validation order requires
+    if (stamps == nullptr || (((uintptr_t)stamps) & 7))
+        return pipegemm::fail(GEMM_ERR_ARG, "gemm_stamped: stamps must be a non-null 8-byte aligned pointer");
+    return pipegemm::run(layout, A, B, C, M, N, K, dtype, block_M, block_N, block_K, num_stages, a_lead, threads,
+                         hip_stream, 0, (unsigned long long *)stamps);
 }
 
 int64_t gemm_lds_bytes(int block_M, int block_N, int block_K, int num_stages, int a_lead, int dtype)

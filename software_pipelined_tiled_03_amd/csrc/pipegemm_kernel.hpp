@@ -86,6 +86,10 @@ struct KernelArgs {
     int group_m;  // tile rows swept before advancing along N (L2 reuse)
     int c_vec;    // 1 when C rows allow 16-byte stores (N % 8 == 0, C 16-byte aligned)
     int relu;     // 1: C = relu(A.B), the fp32 sum s replaced by (s > 0 ? s : +0) before rounding
+    // null, or 6 counters per workgroup (stamp_index): shader-clock cycles at
+    // start, after the prologue, after the K loop and at the end, then the
+    // 100 MHz real-time counter at start and end
+    unsigned long long *stamps;
 };
 
 // ---------------------------------------------------------------------------
@@ -249,25 +253,6 @@ __device__ __forceinline__ void copy_1k(__amdgpu_buffer_rsrc_t rsrc, char *dst, 
 // (their num_records are all below 2^31), so the load returns zero.
 constexpr uint32_t kOOB = 0x80000000u;
 
-// Map the workgroup id to a C tile.  Workgroups are dispatched round-robin
-// over the 8 XCDs (id mod 8), each with its own L2: renumber so that the ids
-// one XCD receives are consecutive, then walk tiles in groups of group_m tile
-// rows so that the workgroups sharing an XCD share A panels and B panels.
-__device__ __forceinline__ void map_tile(const KernelArgs &p, int &tm, int &tn)
-{
-    const int nwg = p.tiles_m * p.tiles_n;
-    const int bid = blockIdx.x;
-    const int xcd = bid & 7, idx = bid >> 3;
-    const int per = nwg >> 3, rem = nwg & 7;
-    const int id = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
-    const int width = p.group_m * p.tiles_n;
-    const int first_m = (id / width) * p.group_m;
-    const int gsize = min(p.tiles_m - first_m, p.group_m);
-    const int in_group = id % width;
-    tm = first_m + in_group % gsize;
-    tn = in_group / gsize;
-}
-
 // Calls f(std::integral_constant<int, i>()) for i = 0 .. N-1, so the body can
 // use i in constant expressions (template arguments of scheduling hints).
 template <class F, int... I>
@@ -370,13 +355,17 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
     constexpr int NACC = MF == 32 ? 16 : 4;  // accumulators per lane per block
 
     extern __shared__ __attribute__((aligned(1024))) char smem[];
+    // clock stamps (scalar reads of the cycle and real-time counters; written
+    // out at the end only when p.stamps is set)
+    const unsigned long long st_c0 = __builtin_amdgcn_s_memtime(), st_t0 = __builtin_amdgcn_s_memrealtime();
+    unsigned long long st_c1 = 0, st_c2 = 0;
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int wm = wave % Cfg::WM, wn = wave / Cfg::WM;
 
     int tm, tn;
-    map_tile(p, tm, tn);
+    map_tile(blockIdx.x, p.tiles_m, p.tiles_n, p.group_m, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
     const int K = p.K, N = p.N, nk = p.nk;
 
@@ -582,6 +571,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
         if constexpr (S == 1) {
             // one slot: the copy of round kt+1 may start only after every wave
             // has finished computing round kt; copy and compute never overlap
+            st_c1 = __builtin_amdgcn_s_memtime();
             for (int kt = 0; kt < nk; ++kt) {
                 issue_a(kt, ring_a, 0, kLA);
                 issue_b(kt, ring_b, 0, kLB);
@@ -608,6 +598,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
                 issue_a(S - 1, ring_a + ring_slot(S - 1, SA) * Cfg::A_BYTES, 0, kLA);
             wait_vmcnt<ring_wait_first(S, LEAD, kLA, kLB)>();
             barrier();
+            st_c1 = __builtin_amdgcn_s_memtime();
             read_operands(ring_a, ring_b, 0, 0);
             if constexpr (kEarlyB) {
                 // the B copies iteration 0 would issue, into the slot no tile used yet
@@ -714,6 +705,12 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
             }
             // no copy may still be writing LDS when the workgroup ends
             wait_vmcnt<0>();
+            // the last iteration's reads of the next (padding) tile are never
+            // used; with the NN form's untracked transposed reads, keep their
+            // destination registers live until the reads have returned, so
+            // the compiler cannot hand them to other values meanwhile
+            sync_operands(0);
+            sync_operands(1);
         }
     };
     // Instantiated rings: the B ring fits in 160 KiB with the A ring, and the
@@ -722,7 +719,8 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
     ((i) >= 1 && ((l) == 0 || ((i) >= 2 && (i) <= kMaxLeadStages)) &&                                   \
      ring_fits_vmcnt((i), (l), Cfg::A_LOADS, Cfg::B_LOADS) &&                                            \
      ring_lds_bytes((i), (l), Cfg::A_BYTES, Cfg::B_BYTES) <= 160 * 1024)
-    switch (p.stages) {
+    // K == 0: no K tile, C = 0 (the accumulators as cleared)
+    if (nk > 0) switch (p.stages) {
 #define PG_STAGES_CASE(i)                                                          \
     case i:                                                                        \
         if (p.a_lead) {                                                            \
@@ -747,67 +745,82 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
     // its own LDS strip so that every global store writes 16 contiguous bytes
     // per lane and whole row segments per instruction, instead of 8 bytes in
     // each of 16 or 32 rows.
+    st_c2 = __builtin_amdgcn_s_memtime();
     wait_vmcnt<0>();
     barrier();
+    // ReLU once over the accumulators, under one uniform branch
+    if (p.relu) {
+#pragma unroll
+        for (int f = 0; f < FM; ++f)
+#pragma unroll
+            for (int g = 0; g < FN; ++g)
+#pragma unroll
+                for (int v = 0; v < NACC; ++v)
+                    acc[f][g][v] = acc[f][g][v] > 0.f ? acc[f][g][v] : 0.f;
+    }
     T *C = (T *)p.C;
     const int M = p.M;
     const int mw = m0 + wm * Cfg::TM, nw = n0 + wn * Cfg::TN;
-    // the fp32 sum of element (block f, g; accumulator v), ReLU applied
-    auto out_value = [&](int f, int g, int v) {
-        float x = acc[f][g][v];
-        if (p.relu)
-            x = x > 0.f ? x : 0.f;
-        return (T)x;
-    };
+    auto out_value = [&](int f, int g, int v) { return (T)acc[f][g][v]; };
     // The workgroup's rows of C as one buffer resource (below 2 GiB, checked
-    // on the host), so a 16-byte store needs one 32-bit offset per lane.
+    // on the host), so a 16-byte store needs one 32-bit offset per lane; a
+    // store to a row past M falls outside it and is dropped.
     const __amdgpu_buffer_rsrc_t c_rs =
         __builtin_amdgcn_make_buffer_rsrc((void *)(C + (size_t)m0 * N), 0, min(BM, M - m0) * N * 2, 0x00020000);
     // 16 bytes (8 columns from n) of row m of C; columns past N are skipped
     auto store_row = [&](int m, int n, i16x8 x) {
-        if (m < M) {
-            short *crow = (short *)(C + (size_t)m * N);
-            if (p.c_vec && n + 7 < N) {
-                // C is written once and is far larger than the L2s: streaming
-                // (nt) at system scope (sc1), so the L2 keeps none of it.
-                // Measured at 4096^3 against a plain store: -1.6 us for nt,
-                // another -1 us for sc1.
+        if (p.c_vec) {
+            // N % 8 == 0: a 16-byte chunk is wholly inside or outside the row.
+            // C is written once and is far larger than the L2s: streaming
+            // (nt) at system scope (sc1), so the L2 keeps none of it.
+            // Measured at 4096^3 against a plain store: -1.6 us for nt,
+            // another -1 us for sc1.
+            if (n < N)
                 __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, x), c_rs, ((m - m0) * N + n) * 2, 0,
                                                        kStoreNtSc1);
-            } else {
+        } else if (m < M) {
+            short *crow = (short *)(C + (size_t)m * N);
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    if (n + e < N)
-                        crow[n + e] = x[e];
-            }
+            for (int e = 0; e < 8; ++e)
+                if (n + e < N)
+                    crow[n + e] = x[e];
         }
     };
     if constexpr (MF == 16) {
         // one strip of 16 rows x TN columns per block row f: lane holds row
-        // lr, columns 16 g + 4 lh .. +3 of block g
-        constexpr int TN = Cfg::TN, CH = TN / 8;
-        static_assert(32 * TN * WAVES <= Cfg::SLOT_BYTES, "strips must fit in one ring slot");
+        // lr, columns 16 g + 4 lh .. +3 of block g.  NF block rows go through
+        // LDS per batch (as many as one ring slot holds for every wave), so a
+        // batch costs one LDS round trip instead of one per block row.
+        constexpr int TN = Cfg::TN, CH = TN / 8, STRIP = 32 * TN;
+        constexpr int NF = epi_batch(FM, Cfg::SLOT_BYTES / (WAVES * STRIP));
+        static_assert(NF >= 1 && FM % NF == 0 && NF * STRIP * WAVES <= Cfg::SLOT_BYTES,
+                      "strips must fit in one ring slot");
         static_assert((16 * CH) % 64 == 0, "whole strip reads");
-        char *strip = smem + wave * 32 * TN;
+        char *strip = smem + wave * NF * STRIP;
 #pragma unroll
-        for (int f = 0; f < FM; ++f) {
+        for (int f0 = 0; f0 < FM; f0 += NF) {
 #pragma unroll
-            for (int g = 0; g < FN; ++g) {
-                typename E::quad v;
+            for (int fl = 0; fl < NF; ++fl)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    v[r] = out_value(f, g, r);
-                *(typename E::quad *)(strip + strip_half_offset<TN>(lr, 2 * g + (lh >> 1), lh & 1)) = v;
-            }
+                for (int g = 0; g < FN; ++g) {
+                    typename E::quad v;
 #pragma unroll
-            for (int i = 0; i < CH / 4; ++i) {
-                const int idx = i * 64 + lane;
-                const int r = idx / CH, c = idx % CH;
-                i16x8 x = *(const i16x8 *)(strip + strip_offset<TN>(r, c));
-                if (r & 1)
-                    x = __builtin_shufflevector(x, x, 4, 5, 6, 7, 0, 1, 2, 3);
-                store_row(mw + f * 16 + r, nw + c * 8, x);
-            }
+                    for (int r = 0; r < 4; ++r)
+                        v[r] = out_value(f0 + fl, g, r);
+                    *(typename E::quad *)(strip + fl * STRIP + strip_half_offset<TN>(lr, 2 * g + (lh >> 1), lh & 1)) =
+                        v;
+                }
+#pragma unroll
+            for (int fl = 0; fl < NF; ++fl)
+#pragma unroll
+                for (int i = 0; i < CH / 4; ++i) {
+                    const int idx = i * 64 + lane;
+                    const int r = idx / CH, c = idx % CH;
+                    i16x8 x = *(const i16x8 *)(strip + fl * STRIP + strip_offset<TN>(r, c));
+                    if (r & 1)
+                        x = __builtin_shufflevector(x, x, 4, 5, 6, 7, 0, 1, 2, 3);
+                    store_row(mw + (f0 + fl) * 16 + r, nw + c * 8, x);
+                }
         }
     } else {
         // G blocks of 32 x 32 at a time (one 32-row strip, 32 G columns)
@@ -842,6 +855,16 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
                 }
             }
         }
+    }
+    if (p.stamps && threadIdx.x == 0) {
+        const unsigned long long c3 = __builtin_amdgcn_s_memtime(), t3 = __builtin_amdgcn_s_memrealtime();
+        unsigned long long *q = p.stamps + stamp_index(blockIdx.x, 0);
+        q[0] = st_c0;
+        q[1] = st_c1;
+        q[2] = st_c2;
+        q[3] = c3;
+        q[4] = st_t0;
+        q[5] = t3;
     }
 }
 

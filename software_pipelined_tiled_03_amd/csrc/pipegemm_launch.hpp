@@ -32,6 +32,7 @@ constexpr int loads_per_wave(int bm, int bn, int bk, int waves)
     X(128, 128, 32, 2, 2)          \
     X(128, 128, 32, 2, 4)          \
     X(128, 128, 64, 2, 2)          \
+    X(128, 128, 64, 2, 4)          \
     X(128, 256, 32, 2, 2)          \
     X(128, 256, 64, 2, 2)          \
     X(128, 256, 64, 2, 4)          \

@@ -12,6 +12,31 @@
 namespace pipegemm {
 
 // ---------------------------------------------------------------------------
+// Workgroup -> C tile.  Workgroups are dispatched round-robin over the 8 XCDs
+// (id mod 8), each with its own L2: the id is renumbered so that the ids one
+// XCD receives are consecutive, and tiles are walked in groups of group_m
+// tile rows (column by column within a group) so that the workgroups sharing
+// an XCD share A panels and B panels.  A bijection from 0 .. tiles_m tiles_n
+// - 1 onto the tiles (the grid is ceil(N / block_N) x ceil(M / block_M)
+// workgroups, chapter 11, section 1.1); enumerated on the CPU.
+PG_HD constexpr void map_tile(int bid, int tiles_m, int tiles_n, int group_m, int &tm, int &tn)
+{
+    const int nwg = tiles_m * tiles_n;
+    const int xcd = bid & 7, idx = bid >> 3;
+    const int per = nwg >> 3, rem = nwg & 7;
+    const int id = xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
+    const int width = group_m * tiles_n;
+    const int first_m = (id / width) * group_m;
+    const int gsize = tiles_m - first_m < group_m ? tiles_m - first_m : group_m;
+    const int in_group = id % width;
+    tm = first_m + in_group % gsize;
+    tn = in_group / gsize;
+}
+
+// Index of counter i (0..5) of workgroup bid in the clock-stamp array.
+PG_HD constexpr int stamp_index(int bid, int i) { return 6 * bid + i; }
+
+// ---------------------------------------------------------------------------
 // K-contiguous tiles (A always; B in the NT form).  Row r holds BK elements,
 // i.e. BK/8 16-byte chunks; logical chunk c of row r is stored at physical
 // chunk c ^ kswz(r).
@@ -230,6 +255,18 @@ template <int TN>
 PG_HD constexpr int strip_half_offset(int r, int c, int h)
 {
     return strip_offset<TN>(r, c) + ((h ^ (r & 1)) << 3);
+}
+
+// Block rows of the 16x16x32 epilogue staged through LDS per batch: the
+// largest divisor of FM that is at most `fit` (the strips one wave's share of
+// a ring slot holds), and at least 1.
+PG_HD constexpr int epi_batch(int FM, int fit)
+{
+    int nf = 1;
+    for (int d = 1; d <= FM; ++d)
+        if (FM % d == 0 && d <= fit)
+            nf = d;
+    return nf;
 }
 
 // ---------------------------------------------------------------------------

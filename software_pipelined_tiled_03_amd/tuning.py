@@ -221,6 +221,33 @@ def tune(A, B, layout="nt", configs=None, warmup=25, reps=100, out=None, stream=
     return TuneResult(cands[best.value], float(ms[best.value]), table)
 
 
+def time_config(A, B, config, layout="nt", warmup=5, reps=30, out=None, stream=None):
+    """Mean milliseconds per launch of one configuration on A, B, timed by the
+    library's own loop (gemm_tune with a single candidate: `warmup`
+    launches, then `reps` back-to-back launches between two HIP events), so a
+    small problem measures its kernels rather than the host's per-call cost.
+    The tile need not divide the problem (edge tiles are masked)."""
+    import torch
+
+    lc = _layout_code(layout)
+    M, K = A.shape
+    N = B.shape[0] if lc == _b.GEMM_NT else B.shape[1]
+    c = dict(DEFAULTS, **config)
+    if out is None:
+        out = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(A.device).cuda_stream
+    arr = (GemmConfig * 1)(GemmConfig(*[c[f] for f in _FIELDS]))
+    st_arr = (ctypes.c_int32 * 1)(_b.GEMM_OK)
+    ms = (ctypes.c_float * 1)()
+    best = ctypes.c_int32(-1)
+    with torch.cuda.device(A.device):
+        st = _lib().gemm_tune(lc, A.data_ptr(), B.data_ptr(), out.data_ptr(), M, N, K, _b._dtype_code(A), arr, st_arr,
+                              1, warmup, reps, stream, ms, ctypes.byref(best))
+    _b._raise_for(st)
+    return float(ms[0])
+
+
 _tuned = {}
 
 

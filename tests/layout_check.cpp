@@ -471,8 +471,64 @@ void check_ring()
     CHECK(ring_lds_bytes(3, 0, 16384, 16384) == 3 * 32768, "no-lead ring is S stages");
 }
 
+// The workgroup -> C tile map is a bijection of 0 .. tiles_m tiles_n - 1 onto
+// the grid, for every grid up to 64 x 64 tiles (group_m = min(tiles_m, 4), as
+// the host sets it), which covers the 4096^3 grids at 256 x 256 (16 x 16) and
+// 128 x 128 (32 x 32) and the 4000 x 5000 grids (16 x 20, 32 x 40).  Also:
+// each XCD (id mod 8) receives consecutive renumbered ids, so with the
+// 4096^3 grid at 256 x 256 an XCD's 32 tiles form a 4 x 8 block (4 A panels,
+// 8 B panels).
+void check_map_tile()
+{
+    std::vector<int> seen;
+    for (int tm_n = 1; tm_n <= 64; ++tm_n)
+        for (int tn_n = 1; tn_n <= 64; ++tn_n) {
+            const int gm = tm_n < 4 ? tm_n : 4;
+            seen.assign(tm_n * tn_n, 0);
+            for (int bid = 0; bid < tm_n * tn_n; ++bid) {
+                int tm = -1, tn = -1;
+                map_tile(bid, tm_n, tn_n, gm, tm, tn);
+                if (tm < 0 || tm >= tm_n || tn < 0 || tn >= tn_n) {
+                    CHECK(false, "map_tile %dx%d: workgroup %d -> (%d,%d) outside the grid", tm_n, tn_n, bid, tm, tn);
+                    continue;
+                }
+                ++seen[tm * tn_n + tn];
+            }
+            for (int t = 0; t < tm_n * tn_n; ++t)
+                CHECK(seen[t] == 1, "map_tile %dx%d: tile (%d,%d) owned by %d workgroups", tm_n, tn_n, t / tn_n,
+                      t % tn_n, seen[t]);
+        }
+    // the XCD blocks of the 4096^3 grid at 256 x 256
+    for (int x = 0; x < 8; ++x) {
+        std::set<int> rows, cols;
+        for (int bid = x; bid < 256; bid += 8) {
+            int tm = 0, tn = 0;
+            map_tile(bid, 16, 16, 4, tm, tn);
+            rows.insert(tm);
+            cols.insert(tn);
+        }
+        CHECK(rows.size() == 4 && cols.size() == 8, "XCD %d of the 16x16 grid spans %zu tile rows and %zu tile "
+              "columns, not 4 x 8", x, rows.size(), cols.size());
+    }
+}
+
+// Epilogue batches: a divisor of FM that fits, and the largest such.
+void check_epi_batch()
+{
+    for (int fm = 1; fm <= 16; ++fm)
+        for (int fit = 0; fit <= 20; ++fit) {
+            const int nf = epi_batch(fm, fit);
+            CHECK(nf >= 1 && fm % nf == 0, "epi_batch(%d,%d) = %d does not divide", fm, fit, nf);
+            CHECK(nf == 1 || nf <= fit, "epi_batch(%d,%d) = %d does not fit", fm, fit, nf);
+            for (int d = nf + 1; d <= fm && d <= fit; ++d)
+                CHECK(fm % d != 0, "epi_batch(%d,%d) = %d, but %d also fits", fm, fit, nf, d);
+        }
+}
+
 int main()
 {
+    check_map_tile();
+    check_epi_batch();
     check_k_tile<32>(256);
     check_k_tile<64>(256);
     check_k_tile<64>(64);

@@ -1,11 +1,20 @@
 """Assembly checks of the built kernels (the gfx950 analogue of the pages'
-look at the generated code, chapter 11 sections 2.1 and 4.3: the pipelined
-loop keeps one wait and one barrier per round, the non-pipelined one two
-barriers, and the wait count grows with the number of stages).
+look at the generated code, chapter 11 sections 2.1 and 4.3, and the
+"expected output" of the num_stages IR-diff and T.Pipelined examples: the
+pipelined loop keeps one wait and one barrier per round, the non-pipelined one
+two barriers, and the wait count grows with the number of stages).
 
-Compiles one kernel translation unit of this repository to gfx950 assembly on
-the CPU (hipcc cross-compiles; no device) and inspects every K loop of one
-instantiation: the dispatch on num_stages gives one loop per built ring."""
+Compiles kernel translation units of this repository to gfx950 assembly on the
+CPU (hipcc cross-compiles; no device) and inspects every K loop of an
+instantiation: the dispatch on num_stages gives one loop per built ring.
+Checked instantiations:
+  - Tile<128,128,32,2,2> (32x32x16 MFMA, 4 waves), every ring it builds;
+  - the headline Tile<256,256,64,2,4> (16x16x32 MFMA, 8 waves): S = 1, 2 and
+    2 + a_lead with early B copies and paired wave-priority changes.
+And for the NN form, whose transposed LDS reads are inline assembly the
+compiler does not track: on every control-flow path, no instruction touches a
+transposed read's destination registers before the next s_waitcnt
+lgkmcnt(0)."""
 import os
 import re
 import subprocess
@@ -19,19 +28,36 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # Tile<128,128,32,2,2> (32x32x16 MFMA): 4 waves, 2 + 2 one-KiB copies per wave per K tile
 KERNEL = "_ZN8pipegemm11gemm_kernelIDF16_Lb0ENS_4TileILi128ELi128ELi32ELi2ELi2ELi32EEELb0EEEvNS_10KernelArgsE"
 LA = LB = 2
+# the headline Tile<256,256,64,2,4> (16x16x32 MFMA): 8 waves, 4 + 4 copies per wave per K tile
+HEADLINE = "_ZN8pipegemm11gemm_kernelIDF16_Lb0ENS_4TileILi256ELi256ELi64ELi2ELi4ELi16EEELb0EEEvNS_10KernelArgsE"
+HLA = HLB = 4
+
+
+def _compile(tmp_path_factory, elem, nn):
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("asm") / ("k_%s_%d.s" % (elem.strip("_"), nn))
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+                    "-packed-fp32-ops", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC, "-DPG_ELEM=" + elem,
+                    "-DPG_NN=%d" % nn, "-DPG_KCHECK=0", "--cuda-device-only", "-S",
+                    os.path.join(CSRC, "pipegemm_kernels.hip"), "-o", str(out)], check=True, capture_output=True)
+    return out.read_text()
 
 
 @pytest.fixture(scope="module")
-def loops(tmp_path_factory):
-    if not os.path.exists(HIPCC):
-        pytest.skip("hipcc not available")
-    out = tmp_path_factory.mktemp("asm") / "k.s"
-    subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-                    "-packed-fp32-ops", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC, "-DPG_ELEM=_Float16",
-                    "-DPG_NN=0", "-DPG_KCHECK=0", "--cuda-device-only", "-S",
-                    os.path.join(CSRC, "pipegemm_kernels.hip"), "-o", str(out)], check=True, capture_output=True)
-    text = out.read_text()
-    start = text.index(KERNEL + ":")
+def nt_f16_asm(tmp_path_factory):
+    return _compile(tmp_path_factory, "_Float16", 0)
+
+
+@pytest.fixture(scope="module")
+def nn_bf16_asm(tmp_path_factory):
+    return _compile(tmp_path_factory, "__bf16", 1)
+
+
+def k_loops(text, kernel, mfma):
+    """Every loop (back edge to a 'Loop Header' label) of one kernel, with its
+    counts and its instructions in order."""
+    start = text.index(kernel + ":")
     end = text.index(".Lfunc_end", start)
     body = text[start:end].splitlines()
     labels = {m.group(1): k for k, l in enumerate(body) for m in [re.match(r"^(\.LBB\d+_\d+):", l)] if m}
@@ -40,15 +66,26 @@ def loops(tmp_path_factory):
         m = re.search(r"s_cbranch_\w+\s+(\.LBB\d+_\d+)", l)
         if m and m.group(1) in labels and labels[m.group(1)] < k and "Loop Header" in body[labels[m.group(1)]]:
             seg = body[labels[m.group(1)]:k + 1]
+            ins = [x.strip() for x in seg if x.strip() and not x.strip().startswith(";") and not x.strip().endswith(":")]
             found.append(dict(
-                barriers=sum(1 for x in seg if re.match(r"\s*s_barrier\b", x)),
-                vmcnt=[int(x) for y in seg for x in re.findall(r"s_waitcnt vmcnt\((\d+)\)", y)],
-                mfma=sum(1 for x in seg if "v_mfma_f32_32x32x16_f16" in x),
-                lds_loads=sum(1 for x in seg if re.search(r"buffer_load_dwordx4\b.*\blds\b", x)),
-                lds_reads=sum(1 for x in seg if "ds_read_b128" in x),
-                valu=sum(1 for x in seg if re.match(r"\s*v_(?!mfma|accvgpr)", x)),
-                text="\n".join(seg)))
+                barriers=sum(1 for x in ins if re.match(r"s_barrier\b", x)),
+                vmcnt=[int(x) for y in ins for x in re.findall(r"s_waitcnt vmcnt\((\d+)\)", y)],
+                mfma=sum(1 for x in ins if mfma in x),
+                lds_loads=sum(1 for x in ins if re.search(r"buffer_load_dwordx4\b.*\blds\b", x)),
+                lds_reads=sum(1 for x in ins if "ds_read_b128" in x),
+                valu=sum(1 for x in ins if re.match(r"v_(?!mfma|accvgpr)", x)),
+                ins=ins, text="\n".join(seg)))
     return found
+
+
+@pytest.fixture(scope="module")
+def loops(nt_f16_asm):
+    return k_loops(nt_f16_asm, KERNEL, "v_mfma_f32_32x32x16_f16")
+
+
+@pytest.fixture(scope="module")
+def headline_loops(nt_f16_asm):
+    return k_loops(nt_f16_asm, HEADLINE, "v_mfma_f32_16x16x32_f16")
 
 
 def expected_rings():
@@ -94,3 +131,105 @@ def test_no_vector_alu_per_copy_in_the_steady_state(loops):
     for l in loops:
         if l["barriers"] == 1:
             assert l["valu"] <= 8, l["text"]
+
+
+# --- the headline instantiation ---------------------------------------------
+
+def test_headline_rings(headline_loops):
+    # 256 x 256 x 64 stages are 64 KiB: S = 1 (64 KiB), S = 2 (128 KiB) and
+    # S = 2 + a_lead (160 KiB) fit the 160 KiB LDS, nothing deeper
+    assert len(headline_loops) == 3
+    by_wait = sorted((l["barriers"], tuple(l["vmcnt"])) for l in headline_loops)
+    # S = 1: two barriers and a full wait; S = 2: one barrier, wait for
+    # everything (ring_wait_steady(2, 0) = 0); S = 2 + a_lead: one barrier,
+    # the leading A tile's 4 copies stay in flight (ring_wait_steady(2, 1, 4, 4))
+    assert by_wait == [(1, (0,)), (1, (HLA,)), (2, (0,))]
+
+
+def test_headline_rounds_copy_read_and_multiply(headline_loops):
+    for l in headline_loops:
+        # each of the 8 waves owns 128 x 64 = 8 x 4 blocks of 16 x 16, 2 k-steps of 32 per K tile
+        assert l["mfma"] == 8 * 4 * 2
+        assert l["lds_loads"] == HLA + HLB                 # one K tile's copies per round
+        assert l["lds_reads"] == (8 + 4) * 2               # A and B fragments of both k-steps
+
+
+def test_headline_early_b_and_priority(headline_loops):
+    lead = [l for l in headline_loops if l["vmcnt"] == [HLA]]
+    assert len(lead) == 1
+    ins = lead[0]["ins"]
+    bar = next(i for i, x in enumerate(ins) if x.startswith("s_barrier"))
+    wait = next(i for i, x in enumerate(ins) if x.startswith("s_waitcnt") and "vmcnt" in x)
+    copies = [i for i, x in enumerate(ins) if re.search(r"buffer_load_dwordx4\b.*\blds\b", x)]
+    # A copies of tile j+2 before the wait, B copies of tile j+2 after the barrier (early B)
+    assert sum(1 for i in copies if i < wait) == HLA
+    assert sum(1 for i in copies if i > bar) == HLB
+    # wave priority: raised and dropped in pairs, and low while waiting
+    prio = [(i, int(x.split()[1])) for i, x in enumerate(ins) if x.startswith("s_setprio")]
+    assert [p for _, p in prio].count(1) == [p for _, p in prio].count(0) >= 1
+    before_wait = [p for i, p in prio if i < wait]
+    assert before_wait and before_wait[-1] == 0, "the wave waits for its copies at priority 0"
+    after_bar = [p for i, p in prio if i > bar]
+    assert after_bar and after_bar[0] == 1, "priority is raised again after the barrier"
+    # 8-wave tiles keep their accumulators in VGPRs: no accumulator copies in the loop
+    assert not any(x.startswith("v_accvgpr") for x in ins)
+
+
+# --- NN form: untracked transposed reads --------------------------------------
+
+def _regs(tok):
+    out = set()
+    for m in re.finditer(r"\bv\[(\d+):(\d+)\]|\bv(\d+)\b", tok):
+        if m.group(3):
+            out.add(int(m.group(3)))
+        else:
+            out.update(range(int(m.group(1)), int(m.group(2)) + 1))
+    return out
+
+
+def tr_read_hazards(text):
+    """(reads, hazards): for each ds_read_b64_tr_b16, follow every control-flow
+    path (fall-through and branch targets) until an s_waitcnt with
+    lgkmcnt(0); a hazard is any instruction on the way that reads or writes
+    one of the read's destination VGPRs.  Paths the dispatch on num_stages
+    makes impossible are followed too, so the check is conservative."""
+    lines = text.splitlines()
+    labels = {m.group(1): i for i, l in enumerate(lines) for m in [re.match(r"^(\.LBB\d+_\d+):", l)] if m}
+    reads = hazards = 0
+    for i, l in enumerate(lines):
+        t = l.strip()
+        if not t.startswith("ds_read_b64_tr_b16"):
+            continue
+        reads += 1
+        dst = _regs(t.split(None, 1)[1].split(",")[0])
+        stack, seen, hit = [i + 1], set(), False
+        while stack and not hit:
+            j = stack.pop()
+            while j < len(lines) and j not in seen:
+                seen.add(j)
+                u = lines[j].strip()
+                j += 1
+                if not u or u.startswith((";", ".")) or u.endswith(":"):
+                    continue
+                if u.startswith("s_waitcnt") and "lgkmcnt(0)" in u:
+                    break
+                if u.startswith("s_endpgm"):
+                    break
+                op = u.split(None, 1)
+                if op[0] == "s_branch":
+                    stack.append(labels[op[1].strip()])
+                    break
+                if op[0].startswith("s_cbranch"):
+                    stack.append(labels[op[1].strip()])
+                    continue
+                if len(op) > 1 and _regs(op[1]) & dst:
+                    hit = True
+                    break
+        hazards += hit
+    return reads, hazards
+
+
+def test_nn_transposed_reads_are_waited_for(nn_bf16_asm):
+    reads, hazards = tr_read_hazards(nn_bf16_asm)
+    assert reads > 1000  # every NN tile and ring issues them
+    assert hazards == 0

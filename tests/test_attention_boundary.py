@@ -71,3 +71,13 @@ def test_grouped_and_causal_configurations_are_valid():
     assert check(B=2, H=32, Hkv=8, Sq=2048, Skv=2048, dtype=BF16, causal=1) == pg.GEMM_OK
     assert check(Sq=1, Skv=1) == pg.GEMM_OK
     assert check(Sq=300, Skv=777) == pg.GEMM_OK
+
+
+def test_scale_must_be_zero_or_positive_and_finite():
+    # rejected as an argument error before any device is touched: the
+    # pointers below are aligned placeholders that are never dereferenced
+    fake = [0x100000, 0x200000, 0x300000, 0x400000]
+    for scale in (-1.0, -1e-30, float("nan"), float("inf"), float("-inf")):
+        st = pg.attn_fwd_raw(*fake, 1, 1, 1, 128, 128, 128, F16, 0, scale, 128, 64, 2, 256, None)
+        assert st == pg.GEMM_ERR_ARG, scale
+        assert "scale" in pg.last_error()

@@ -68,3 +68,41 @@ def test_profiled_traffic_is_used_only_for_the_profiled_sources(monkeypatch):
     assert bench.measured_traffic(*args) == int(fields["hbm_bytes_per_launch"])
     # compulsory traffic 2(MK + NK + MN) is a lower bound for what a launch moves
     assert int(fields["hbm_bytes_per_launch"]) >= 2 * 3 * 4096 * 4096
+
+
+def test_shape_ceiling_counts_rounds_of_the_compute_units():
+    # 4096^3 at 256 x 256: 256 tiles, one round, no padding
+    assert bench.shape_ceiling(4096, 4096, 4096, (256, 256, 64)) == pytest.approx(bench.PEAK_TFLOPS)
+    # 1024^3 at 128 x 128: 64 tiles on 256 compute units
+    assert bench.shape_ceiling(1024, 1024, 1024, (128, 128, 32)) == pytest.approx(bench.PEAK_TFLOPS * 0.25)
+    # 4000 x 5000 at 256 x 256: 16 x 20 = 320 tiles take two rounds (the second a quarter full),
+    # times the useful fraction of the padded work
+    useful = 4000 * 5000 * 3000 / (4096 * 5120 * 3008)
+    assert bench.shape_ceiling(4000, 5000, 3000, (256, 256, 64)) == pytest.approx(
+        bench.PEAK_TFLOPS * 320 / 512 * (4000 * 5000 * 3000) / (4096 * 5120 * 3008))
+    assert bench.shape_ceiling(4000, 5000, 3000, (128, 128, 32)) == pytest.approx(bench.PEAK_TFLOPS * useful)
+    # 512 x 512 x 65536 at 128 x 128: 16 workgroups
+    assert bench.shape_ceiling(512, 512, 65536, (128, 128, 32)) == pytest.approx(bench.PEAK_TFLOPS / 16)
+
+
+def test_stamp_summary_reduces_clock_phases_and_residency():
+    import torch
+
+    # 16 workgroups, 2 GHz everywhere but XCD 3 at 1.5 GHz; 1000 cycles of
+    # prologue, 64000 of loop (nk = 64), 2000 of epilogue; 10 us of real time
+    # at 2 GHz, all starting together
+    rows = []
+    for w in range(16):
+        f = 1.5 if w % 8 == 3 else 2.0
+        total = 67000
+        rt = total / f / 10.0  # 10 ns ticks
+        rows.append([0, 1000, 65000, total, 100, 100 + rt])
+    st = bench.stamp_summary(torch.tensor(rows, dtype=torch.float64).to(torch.int64), 64, flops=2.0 * 256 * 4096 * 67000,
+                             ms=67000 / 2.0 / 1e6 * 1.0)
+    assert st["clock_ghz_per_xcd"][3] == pytest.approx(1.5, abs=1e-3)
+    assert st["clock_ghz_per_xcd"][0] == pytest.approx(2.0, abs=1e-3)
+    assert st["clock_ghz_min_xcd"] == pytest.approx(1.5, abs=1e-3)
+    assert st["loop_cycles_per_k_tile"] == pytest.approx(1000.0)
+    assert st["prologue_us"] == pytest.approx(0.5, abs=1e-3)      # 1000 cycles at 2 GHz (median)
+    # 16 workgroups on 256 compute units: 1/16 resident per CU on average over the span
+    assert st["wgs_resident_per_cu"] == pytest.approx(16 / 256 * (14 * 33.5 + 2 * 44.667) / 16 / 44.667, abs=0.01)

@@ -25,7 +25,8 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(
         ["gemm_nt", "gemm_nn", "gemm_nt_relu", "gemm_nn_relu", "gemm_lds_bytes", "gemm_lds_budget", "gemm_check",
-         "gemm_last_error", "gemm_configs", "gemm_prune", "gemm_rank", "gemm_tune", "gemm_default_config"])
+         "gemm_last_error", "gemm_configs", "gemm_prune", "gemm_rank", "gemm_tune", "gemm_default_config",
+         "gemm_stamped"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -164,6 +165,21 @@ def test_no_device_reported_as_hip_error():
     assert pg.gemm_nt_raw(None, None, None, -1, 4, 8, F16, 128, 128, 32, 2, 0, 256, None) == pg.GEMM_ERR_ARG
     assert pg.gemm_nt_raw(16, 16, 16, 4, 4, 8, F16, 128, 128, 32, 2, 0, 256, None) == pg.GEMM_ERR_HIP
     assert pg.gemm_nt_raw(16, 16, 16, 4, 4, 8, F16, 128, 128, 32, 1, 1, 256, None) == pg.GEMM_ERR_ARG
+
+
+def test_stamped_entry_point_arguments():
+    # a null or misaligned stamp array is an argument error, reported before
+    # the budget (validation order), and without touching a device
+    st = pg.gemm_stamped_raw(pg.GEMM_NT, 16, 16, 16, 4096, 4096, 4096, F16, 256, 256, 64, 4, 0, 512, None, None)
+    assert st == pg.GEMM_ERR_ARG and "stamps" in pg.last_error()
+    st = pg.gemm_stamped_raw(pg.GEMM_NT, 16, 16, 16, 4096, 4096, 4096, F16, 256, 256, 64, 2, 1, 512, None, 0x1004)
+    assert st == pg.GEMM_ERR_ARG
+    # otherwise it validates exactly as gemm_nt (the launch budget comes from
+    # the device, so on a host without one a valid call ends in GEMM_ERR_HIP)
+    import torch
+    if not torch.cuda.is_available():
+        st = pg.gemm_stamped_raw(pg.GEMM_NT, 16, 16, 16, 4096, 4096, 4096, F16, 256, 256, 64, 2, 1, 512, None, 0x1000)
+        assert st == pg.GEMM_ERR_HIP
 
 
 def test_size_limits_of_the_32_bit_offsets():

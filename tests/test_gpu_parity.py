@@ -187,6 +187,7 @@ def test_one_gpu_share_512x4096x4096(oracle_gemm):
 # Every built tile, both layouts and dtypes, on a shape ragged in M, N and K
 
 TILES = [(64, 128, 64, 256), (128, 128, 32, 128), (128, 128, 32, 256), (128, 128, 32, 512), (128, 128, 64, 256),
+         (128, 128, 64, 512),
          (128, 256, 32, 256), (128, 256, 64, 256), (128, 256, 64, 512), (256, 128, 32, 256), (256, 128, 32, 512),
          (256, 128, 64, 256),
          (256, 256, 32, 256), (256, 256, 32, 512), (256, 256, 64, 256), (256, 256, 64, 512)]
@@ -234,6 +235,26 @@ def test_k_zero_writes_zeros():
     pg.gemm_nt(dA, dB, out=out, block=(128, 128, 32), num_stages=2)
     torch.cuda.synchronize()
     assert bool((out == 0).all())
+
+
+@pytest.mark.parametrize("block,stages,threads,lead", [((128, 128, 32), 3, 256, 0), ((256, 256, 64), 2, 512, 1),
+                                                       ((128, 128, 32), 1, 256, 0)])
+def test_stamped_launch_writes_the_same_c_and_sane_counters(block, stages, threads, lead):
+    w = inputs.workload("nt_f16_1024")
+    A, B = w.make()
+    dA, dB = dev(A, F16).view(w.M, w.K), dev(B, F16).view(w.N, w.K)
+    plain = pg.gemm_nt(dA, dB, block=block, num_stages=stages, threads=threads, a_lead=lead)
+    C, stamps = pg.gemm_stamped(pg.GEMM_NT, dA, dB, block=block, num_stages=stages, threads=threads, a_lead=lead)
+    torch.cuda.synchronize()
+    assert torch.equal(plain.view(torch.int16), C.view(torch.int16))
+    grid = (w.M // block[0]) * (w.N // block[1])
+    s = stamps.view(-1, 6).cpu().numpy().astype(np.int64)
+    assert s.shape == (grid, 6)
+    # cycles: start <= after prologue <= after the K loop <= end; real time advances
+    assert (s[:, 0] <= s[:, 1]).all() and (s[:, 1] <= s[:, 2]).all() and (s[:, 2] <= s[:, 3]).all()
+    assert (s[:, 4] < s[:, 5]).all()
+    clk = (s[:, 3] - s[:, 0]) / (s[:, 5] - s[:, 4]) * 0.1   # GHz
+    assert 0.3 < float(np.median(clk)) < 3.0
 
 
 def test_empty_m_or_n_is_a_noop():
