@@ -233,3 +233,26 @@ def test_nn_transposed_reads_are_waited_for(nn_bf16_asm):
     reads, hazards = tr_read_hazards(nn_bf16_asm)
     assert reads > 1000  # every NN tile and ring issues them
     assert hazards == 0
+
+
+# --- the register table the knee analysis uses ---------------------------------
+
+def _reg_counts(text):
+    out = {}
+    for m in re.finditer(r"\.agpr_count:\s+\d+.*?\.name:\s+(\S+).*?\.vgpr_count:\s+(\d+)", text, re.S):
+        t = re.search(r"TileILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi\d+", m.group(1))
+        bm, bn, bk, wm, wn = (int(x) for x in t.groups())
+        out[(bm, bn, bk, 64 * wm * wn)] = int(m.group(2))
+    return out
+
+
+def test_knee_register_table_matches_the_builds(nt_f16_asm, nn_bf16_asm):
+    from oracle import knee
+
+    nt, nn = _reg_counts(nt_f16_asm), _reg_counts(nn_bf16_asm)
+    assert set(nt) == set(nn) == set(knee.REG_COUNT)
+    for key, v in knee.REG_COUNT.items():
+        assert v == max(nt[key], nn[key]), key
+        # the occupancy the table implies is the same for every build of the tile
+        for regs in (nt[key], nn[key]):
+            assert 512 // (-(-regs // 8) * 8) == knee.reg_waves_per_simd(*key), key
