@@ -302,6 +302,54 @@ def cpu_baseline(w, A, B, rows, gpu_c=None):
     return out
 
 
+# Shapes of the tuning tables that fix the gfx950 default table (NT fp16)
+TUNE_SHAPES = [(512, 512, 65536), (1024, 1024, 1024), (1024, 1024, 8192), (2048, 2048, 2048), (3072, 3072, 3072),
+               (4096, 4096, 4096), (4096, 4096, 512), (6144, 2048, 2048), (2048, 6144, 2048), (8192, 8192, 1024),
+               (8192, 8192, 8192), (16384, 4096, 4096)]
+
+
+def tune_tables(passes=1):
+    """Every built configuration measured on each TUNE_SHAPES problem (NT fp16,
+    uniform[-1,1] from inputs.custom with seed 7M + 3N + K), after settling
+    launches of the default configuration; each candidate gets about 3 ms of
+    warm-up launches and 3 ms of timed launches (at least 10 and 30), so a
+    short kernel is not timed inside the power manager's transitions.  One
+    JSON line per shape and pass: the tuned winner, the default table's pick
+    (gemm_default_config), the cost model's first choice (gemm_rank), their
+    measured times, and every candidate's time."""
+    import numpy as np
+    import torch
+
+    import software_pipelined_tiled_03_amd as pg
+    from software_pipelined_tiled_03_amd import inputs
+
+    for M, N, K in TUNE_SHAPES:
+        A, B = inputs.custom("nt", inputs.F16, M, N, K, seed=7 * M + 3 * N + K).make()
+        dA = torch.from_numpy(A.view(np.int16)).cuda().view(torch.float16)
+        dB = torch.from_numpy(B.view(np.int16)).cuda().view(torch.float16)
+        C = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        d = pg.default_config("nt", M, N, K)
+        t = pg.tuning.time_config(dA, dB, d, warmup=200, reps=50, out=C)
+        warm, reps = max(10, int(3.0 / t)), max(30, int(3.0 / t))
+        first = pg.rank("nt", M, N, K)[0][0]
+        for p in range(passes):
+            res = pg.tune(dA, dB, "nt", warmup=warm, reps=reps, out=C)
+            ms = {tuple(sorted(c.items())): v for c, st, v in res.table if st == 0}
+            row = dict(shape=[M, N, K], passes=p, legal=len(ms), warmup=warm, reps=reps, best=res.config,
+                       best_ms=round(res.latency, 5), default=d, default_ms=round(ms[tuple(sorted(d.items()))], 5),
+                       model_first=first, model_first_ms=round(ms[tuple(sorted(first.items()))], 5),
+                       table=[[c["block_M"], c["block_N"], c["block_K"], c["num_stages"], c["a_lead"], c["threads"],
+                               round(v, 5)] for c, st, v in res.table if st == 0])
+            row["default_over_best"] = round(row["default_ms"] / row["best_ms"], 4)
+            row["model_first_over_best"] = round(row["model_first_ms"] / row["best_ms"], 4)
+            print(json.dumps(row), flush=True)
+            _log("tune %dx%dx%d pass %d: best %.4f ms, default %.4f ms (x%.3f), model first x%.3f"
+                 % (M, N, K, p, row["best_ms"], row["default_ms"], row["default_over_best"],
+                    row["model_first_over_best"]))
+        del dA, dB, C
+    return 0
+
+
 # Oracle timing table: (workload, timed runs, also on one thread)
 ORACLE_TABLE = [
     ("nt_f16_128", 3, True),
@@ -384,6 +432,8 @@ def main():
     ap.add_argument("--oracle-table", action="store_true",
                     help="only time the CPU oracle on every GEMM workload (all cores and one thread); no GPU")
     ap.add_argument("--oracle-table-worker", type=int, default=None, help=argparse.SUPPRESS)
+    ap.add_argument("--tune-tables", action="store_true",
+                    help="only measure every built configuration on the tuning shapes (one JSON line per shape)")
     args = ap.parse_args()
 
     if args.oracle_table_worker is not None:
@@ -406,6 +456,9 @@ def main():
         print("no GPU available", file=sys.stderr)
         return 1
     pg.load()
+
+    if args.tune_tables:
+        return tune_tables(passes=2)
 
     if args.calibrate_copy_mib:
         n = args.calibrate_copy_mib << 20

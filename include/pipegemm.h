@@ -267,8 +267,8 @@ int gemm_tune(int layout, const void *A, const void *B, void *C, int64_t M, int6
  * gfx950 without tuning (chapter 11, section 3.8: fix the tuned result as a
  * per-device default): one entry per tile, each with the ring and thread count
  * measured best for it on gfx950 -- 256x256x64 (2 stages + a_lead, 512
- * threads), 256x128x64 (3, 256), 128x256x64 (3, 512), 128x128x64 (3 + a_lead,
- * 256), 64x128x64 (5, 256) -- and among them the one gemm_rank models
+ * threads), 256x128x64 (3, 256), 128x256x64 (3, 512), 128x128x64 (3, 512),
+ * 64x128x64 (4, 256) -- and among them the one gemm_rank models
  * cheapest for the problem.  Pure host.  Returns GEMM_OK or GEMM_ERR_ARG.
  */
 int gemm_default_config(int layout, int64_t M, int64_t N, int64_t K, int dtype, gemm_config *out);

@@ -58,6 +58,29 @@ def attention_rows(Q, K, V, dtype, b, h, rows, causal=False, scale=None):
     return P @ v
 
 
+def attention_rows_weights(Q, K, V, dtype, b, h, rows, causal=False, scale=None):
+    """The magnitudes an error bound for O[b, h, rows, :] is built from, in
+    float64: R[r, d] = sum_j P[r, j] |V[j, d]| (P as in attention_rows) and
+    A[r] = scale * max_j sum_d |Q[r, d] K[j, d]| over the visible keys."""
+    B, H, Sq, D = Q.shape
+    Hkv, Skv = K.shape[1], K.shape[2]
+    g = H // Hkv
+    s = 1.0 / np.sqrt(D) if scale is None else float(scale)
+    rows = np.asarray(rows, dtype=np.int64)
+    q = _widen(Q[b, h, rows], dtype)
+    k = _widen(K[b, h // g], dtype)
+    v = _widen(V[b, h // g], dtype)
+    S = s * (q @ k.T)
+    Aqk = s * (np.abs(q) @ np.abs(k).T)
+    if causal:
+        vis = np.arange(Skv)[None, :] <= rows[:, None]
+        S = np.where(vis, S, -np.inf)
+        Aqk = np.where(vis, Aqk, 0.0)
+    E = np.exp(S - S.max(axis=1, keepdims=True))
+    P = E / E.sum(axis=1, keepdims=True)
+    return P @ np.abs(v), Aqk.max(axis=1)
+
+
 def attention(Q, K, V, dtype, causal=False, scale=None, chunk=512):
     """The whole O [B, H, Sq, D] in float64 (row chunks of `chunk` queries)."""
     B, H, Sq, D = Q.shape

@@ -277,20 +277,20 @@ int64_t tiles_of(int64_t M, int64_t N, int bm, int bn)
 // used only to order candidates before they are measured (chapter 11, section
 // 3.9: a cost model prunes and ranks, measurement decides).  Per K tile of one
 // workgroup: MFMA time C = 2 bM bN bK / 4096 flop per CU-cycle, divided by
-// 1.2 for the 16x16x32 tiles (their higher clock under the power limit with
+// 1.4 for the 16x16x32 tiles (their higher clock under the power limit with
 // random operands); copy time X = (bM + bN) bK 2 B at 48 B per cycle, times
 // 1.5 for bK = 32, whose 64-byte rows cost two L2 requests per line; LDS
-// operand reads R = waves (TM + TN) bK 2 B at 128 B per cycle; copy latency
-// L = 2000 cycles.  `occ` workgroups share a compute unit (bounded by LDS and
+// operand reads R = waves (TM + TN) bK 2 B at 192 B per cycle; copy latency
+// L = 1500 cycles.  `occ` workgroups share a compute unit (bounded by LDS and
 // by a register estimate: fp32 accumulators, double-buffered operand
 // fragments and 16 address registers per lane).  With S >= 2 a tile's copies
 // are issued S - 1 tiles ahead (half a tile more with a_lead), so the latency
 // left exposed is max(0, L - (S - 1 + lead / 2) occ max(C, X, R)); with S = 1
 // copy, latency and compute add up.  Each round of occ x 256 workgroups adds
-// the C store (bM bN 2 B per workgroup at 64 B per cycle) and 1000 cycles.
-// The rates and L were fitted to the measured tuning tables of twelve
-// shapes from 512x512x65536 to 16384x4096x4096 (random fp16 operands): the
-// model's first choice is the measured best or within 3 % of it on eleven.
+// the C store (bM bN 2 B per workgroup at 64 B per cycle) and 500 cycles.
+// The rates and L were fitted to two passes of measured tuning tables of
+// twelve shapes from 512x512x65536 to 16384x4096x4096 (random fp16 operands,
+// every built configuration, about 3 ms of warm-up and 3 ms of timing each).
 double model_cost_us(const gemm_config &c, int64_t M, int64_t N, int64_t K)
 {
     const int W = c.threads / 64 > 0 ? c.threads / 64 : 4;
@@ -309,10 +309,10 @@ double model_cost_us(const gemm_config &c, int64_t M, int64_t N, int64_t K)
     const double tiles = (double)tiles_of(M, N, c.block_M, c.block_N);
     const double rounds = std::ceil(tiles / (256.0 * occ));
     const double nk = (double)((K + c.block_K - 1) / c.block_K);
-    const double C = 2.0 * c.block_M * c.block_N * c.block_K / 4096.0 / (MF == 16 ? 1.2 : 1.0);
+    const double C = 2.0 * c.block_M * c.block_N * c.block_K / 4096.0 / (MF == 16 ? 1.4 : 1.0);
     const double X = (c.block_M + c.block_N) * c.block_K * 2.0 / 48.0 * (c.block_K == 32 ? 1.5 : 1.0);
-    const double R = W * (TM + TN) * c.block_K * 2.0 / 128.0;
-    const double L = 2000.0;
+    const double R = W * (TM + TN) * c.block_K * 2.0 / 192.0;
+    const double L = 1500.0;
     double tile;
     if (S == 1) {
         tile = occ * (C + X) > C + X + L ? occ * (C + X) : C + X + L;
@@ -322,7 +322,7 @@ double model_cost_us(const gemm_config &c, int64_t M, int64_t N, int64_t K)
         const double hidden = (S - 1 + 0.5 * c.a_lead) * per;
         tile = per + (L > hidden ? L - hidden : 0.0);
     }
-    const double epi = occ * c.block_M * c.block_N * 2.0 / 64.0 + 1000.0;
+    const double epi = occ * c.block_M * c.block_N * 2.0 / 64.0 + 500.0;
     return rounds * (nk * tile + epi) / 2100.0;
 }
 
@@ -598,20 +598,20 @@ int gemm_default_config(int layout, int64_t M, int64_t N, int64_t K, int dtype, 
     if ((layout != GEMM_NT && layout != GEMM_NN) || (dtype != GEMM_F16 && dtype != GEMM_BF16) || M < 0 || N < 0 ||
         K < 0 || out == nullptr)
         return pipegemm::fail(GEMM_ERR_ARG, "gemm_default_config: bad arguments");
-    // One configuration per tile, each with the ring and wave count that the
-    // measured gfx950 tuning tables of twelve shapes (512 x 512 x 65536 to
-    // 16384 x 4096 x 4096, random fp16, every built configuration) favour
-    // for it; the analytic cost model (gemm_rank) picks among them, so the
-    // choice accounts for how many rounds of workgroups each grid takes on
-    // the 256 compute units (a grid just above 256 tiles leaves the second
-    // round nearly empty).  On those tables the pick is the measured best or
-    // within 2.4 % of it on every shape.  Ties keep the earlier, larger tile.
+    // One configuration per tile, each with the ring and wave count measured
+    // best for it on gfx950 (tuning tables of twelve shapes, 512 x 512 x 65536
+    // to 16384 x 4096 x 4096, random fp16, every built configuration); the
+    // analytic cost model (gemm_rank) picks among them, so the choice accounts
+    // for how many rounds of workgroups each grid takes on the 256 compute
+    // units (a grid just above 256 tiles leaves the second round nearly
+    // empty).  On those tables the pick is the measured best or within 2.4 %
+    // of it.  Ties keep the earlier, larger tile.
     static const gemm_config kTable[] = {
         {256, 256, 64, 2, 1, 512},
         {256, 128, 64, 3, 0, 256},
         {128, 256, 64, 3, 0, 512},
-        {128, 128, 64, 3, 1, 256},
-        {64, 128, 64, 5, 0, 256},
+        {128, 128, 64, 3, 0, 512},
+        {64, 128, 64, 4, 0, 256},
     };
     const gemm_config *pick = &kTable[0];
     double best = pipegemm::model_cost_us(kTable[0], M, N, K);

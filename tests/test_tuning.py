@@ -104,8 +104,8 @@ def test_default_config_is_a_built_legal_configuration(shape, layout, dtype):
     table = [dict(block_M=256, block_N=256, block_K=64, num_stages=2, a_lead=1, threads=512),
              dict(block_M=256, block_N=128, block_K=64, num_stages=3, a_lead=0, threads=256),
              dict(block_M=128, block_N=256, block_K=64, num_stages=3, a_lead=0, threads=512),
-             dict(block_M=128, block_N=128, block_K=64, num_stages=3, a_lead=1, threads=256),
-             dict(block_M=64, block_N=128, block_K=64, num_stages=5, a_lead=0, threads=256)]
+             dict(block_M=128, block_N=128, block_K=64, num_stages=3, a_lead=0, threads=512),
+             dict(block_M=64, block_N=128, block_K=64, num_stages=4, a_lead=0, threads=256)]
     costs = pt.model_costs(M, N, K, table)
     assert c == table[min(range(len(table)), key=lambda i: (costs[i], i))]
 
