@@ -510,7 +510,12 @@ def main():
                               wgs_resident_per_cu=st["wgs_resident_per_cu"],
                               copy_bytes_per_cycle_per_wg=round((block[0] + block[1]) * block[2] * 2
                                                                 / st["loop_cycles_per_k_tile"], 2),
-                              prologue_us=st["prologue_us"], epilogue_us=st["epilogue_us"])
+                              prologue_us=st["prologue_us"], epilogue_us=st["epilogue_us"],
+                              # the stamped launch's own span (first workgroup start to last
+                              # workgroup end): kernel time without launch gaps, which set
+                              # `us` for the smallest shapes
+                              kernel_us=st["wg_span_us"],
+                              tflops_kernel=round(sflops / st["wg_span_us"] / 1e6, 1) if st["wg_span_us"] else None)
                 _log("sweep %s S=%s: %.1f TFLOP/s at %.2f GHz, %.0f cycles per K tile"
                      % (label, d, sflops / ms / 1e9, st["clock_ghz"], st["loop_cycles_per_k_tile"]))
             sweep[label] = row
