@@ -420,6 +420,7 @@ def main():
                     help="back-to-back launches of the timed configuration before its warmup (power settling)")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-attention", action="store_true")
+    ap.add_argument("--attention", action="store_true", help="run the attention sweep even with --no-sweep")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096)
     ap.add_argument("--no-clock", action="store_true", help="skip the clock-stamped launches after the headline")
@@ -588,7 +589,7 @@ def main():
         _log("per launch: warm median %.4f ms (min %.4f, p90 %.4f); cold median %.4f ms"
              % (warm["median_ms"], warm["min_ms"], warm["p90_ms"], cold["median_ms"]))
 
-    attn = None if args.no_attention or args.no_sweep else attention_sweep()
+    attn = attention_sweep() if args.attention or not (args.no_attention or args.no_sweep) else None
 
     # the fused GEMM+ReLU epilogue in the same configuration
     relu_ms = time_gemm(fn, dA, dB, C, block, stages, threads, steps=max(10, args.steps // 2), warmup=args.warmup,

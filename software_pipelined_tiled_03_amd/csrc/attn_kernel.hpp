@@ -13,8 +13,12 @@
 //   S^T = K Q^T        v_mfma_f32_32x32x16 with the K fragment first, so each
 //                      lane ends with one query's scores for 16 of every 32
 //                      keys (its partner lane l ^ 32 holds the other 16);
-//   online softmax     running max m and sum l per query, in fp32, lane-local
-//                      plus one exchange with the partner lane;
+//   online softmax     reference max m and sum l per query, in fp32,
+//                      lane-local plus one exchange with the partner lane;
+//                      m lags the running max by up to 8 in the base-2
+//                      exponent (any reference gives the same quotient), so
+//                      O is rescaled only when it moves; l sums the P values
+//                      after rounding, as the second product sees them;
 //   O^T += V^T P^T     P goes from the S^T accumulator to the second MFMA
 //                      operand with no exchange: the key order it is left in
 //                      is the order the V^T fragment is read in (any common
@@ -59,6 +63,35 @@ struct AttnTile {
     static_assert(QB == 1 || QB == 2, "one or two 32-query blocks per wave");
     static_assert(K_BYTES % (1024 * WAVES) == 0 && K_LOADS >= 1, "whole 1 KiB copies per wave");
 };
+
+// ds_read_b64_tr_b16 at addr + OFF, with OFF in the instruction's 16-bit
+// offset field.  The read is inline assembly for the reason ds_read_tr16_b64
+// gives (the builtin would make the compiler wait for every copy in flight),
+// and the compiler cannot fold constants into an inline-assembly address:
+// without the field every read costs one more vector add (measured 4 % of
+// the attention loop's time at 4096 keys).
+template <int OFF>
+__device__ __forceinline__ i16x4 ds_read_tr16_b64_at(const char *addr)
+{
+    static_assert(OFF >= 0 && OFF < 65536, "ds offset field is 16 bits");
+    i16x4 v;
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char *)addr;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(lds_addr), "i"(OFF) : "memory");
+    return v;
+}
+
+// c + a + b with a, b in the input dtype (v_dot2c_f32_{f16,bf16} against
+// (1, 1): exact products, fp32 accumulation)
+__device__ __forceinline__ float dot2_ones(_Float16 a, _Float16 b, float c)
+{
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2(h2{a, b}, h2{(_Float16)1.0f, (_Float16)1.0f}, c, false);
+}
+__device__ __forceinline__ float dot2_ones(__bf16 a, __bf16 b, float c)
+{
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(b2{a, b}, b2{(__bf16)1.0f, (__bf16)1.0f}, c, false);
+}
 
 template <class T, class Cfg>
 __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
@@ -158,14 +191,24 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
             kf[kb] = *(const frag *)(slot + k_rd[ds] + kb * 32 * 128);
     };
     // V^T fragment (first operand of O^T): column d = 32 db + lr, keys in the
-    // order P is held in (two transposed reads).
-    auto read_v = [&](const char *slot, int ks, frag (&vf)[DB]) __attribute__((always_inline)) {
+    // order P is held in (two transposed reads).  The k-step ks moves every
+    // read by 32 D ks bytes (v_tr_offset), which goes into the instruction's
+    // offset field with the K part of the slot; the lane part is computed
+    // once per slot.
+    int v_rd[DB][2];
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+            v_rd[db][r] = v_tr_offset<D>(lane, 0, 32 * db, r);
+    auto read_v = [&](const char *slot, auto ks_c, frag (&vf)[DB]) __attribute__((always_inline)) {
+        constexpr int OFF = Cfg::K_BYTES + 32 * D * decltype(ks_c)::value;
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             i16x8 out;
 #pragma unroll
             for (int r = 0; r < 2; ++r) {
-                const i16x4 v = ds_read_tr16_b64(slot + Cfg::K_BYTES + v_tr_offset<D>(lane, ks, 32 * db, r));
+                const i16x4 v = ds_read_tr16_b64_at<OFF>(slot + v_rd[db][r]);
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     out[4 * r + e] = v[e];
@@ -191,12 +234,14 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
     }
     const float sl2 = p.scale_log2;
 
-    // One key tile j in `slot`: S^T, softmax, O^T.  The copies of tile cj into
-    // `cslot` (if any) are spread over the two MFMA phases: K pieces among the
-    // S^T k-steps, V pieces among the O^T k-steps.
-    auto compute_tile = [&](int j, const char *slot, int cj, char *cslot, auto copies_c) __attribute__((always_inline)) {
+    // The three phases of one key tile j: S^T = K Q^T into `sacc`, the
+    // online softmax of `sacc` into `pf`, O^T += V^T P^T.  The copies of tile
+    // cj into `cslot` (if any) are spread over the two MFMA phases: K pieces
+    // among the S^T k-steps, V pieces among the O^T k-steps.
+    using SAcc = f32x16[KB][QB];
+    using PFrag = frag[KS][QB];
+    auto s_phase = [&](SAcc &sacc, const char *slot, int cj, char *cslot, auto copies_c) __attribute__((always_inline)) {
         constexpr bool copies = decltype(copies_c)::value;
-        f32x16 sacc[KB][QB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
@@ -219,7 +264,8 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
                 for (int qb = 0; qb < QB; ++qb)
                     sacc[kb][qb] = E::mfma(kf[ds & 1][kb], qf[qb][ds], sacc[kb][qb]);
         });
-
+    };
+    auto softmax = [&](SAcc &sacc, PFrag &pf, int j) __attribute__((always_inline)) {
         // mask: keys past the query (causal) or past Skv
         const int key0 = j * BN;
         if ((p.causal && key0 + BN - 1 > q0w) || key0 + BN > Skv) {
@@ -232,11 +278,13 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
                         const int key = key0 + 32 * kb + 8 * (v >> 2) + 4 * lh + (v & 3);
                         if ((p.causal && key > q0w + 32 * qb + lr) || key >= Skv)
                             sacc[kb][qb][v] = -INFINITY;
+                        // one compare and select at a time, so the
+                        // scheduler does not hold every lane mask in SGPRs
+                        __builtin_amdgcn_sched_barrier(0);
                     }
         }
         // online softmax per query block (base-2 exponentials of
         // scale x log2(e) x score)
-        frag pf[KS][QB];
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
             float mx = sacc[0][qb][0];
@@ -246,36 +294,49 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
                 for (int v = 0; v < 16; ++v)
                     mx = fmaxf(mx, sacc[kb][qb][v]);
             mx = fmaxf(mx, __shfl_xor(mx, 32));
-            const float m_new = fmaxf(m_run[qb], mx);  // finite: every query sees key 0 in tile 0
-            const float alpha = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * sl2);
-            const float mb = m_new * sl2;
+            // the reference max moves only when some query's max has grown by
+            // more than 8 in the base-2 exponent: the exponentials then stay
+            // at most 256, far inside the input dtype's range, and O and l
+            // are rescaled on few tiles (measured: 2-7 % faster at 4096 keys)
+            if (__any((mx - m_run[qb]) * sl2 > 8.0f)) {
+                const float m_new = fmaxf(m_run[qb], mx);  // finite: every query sees key 0 in tile 0
+                const float alpha = __builtin_amdgcn_exp2f((m_run[qb] - m_new) * sl2);
+                l_run[qb] *= alpha;
+                m_run[qb] = m_new;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        oacc[db][qb][v] *= alpha;
+            }
+            const float mb = m_run[qb] * sl2;
             float rs = 0.0f;
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
                 for (int jj = 0; jj < 8; ++jj) {
                     const float e = __builtin_amdgcn_exp2f(fmaf(sacc[ks >> 1][qb][8 * (ks & 1) + jj], sl2, -mb));
-                    rs += e;
                     pf[ks][qb][jj] = (T)e;
                 }
+            // the row sum of the rounded P, two at a time (exact products, fp32 sum)
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int jj = 0; jj < 8; jj += 2)
+                    rs = dot2_ones(pf[ks][qb][jj], pf[ks][qb][jj + 1], rs);
             rs += __shfl_xor(rs, 32);
-            l_run[qb] = l_run[qb] * alpha + rs;
-            m_run[qb] = m_new;
-#pragma unroll
-            for (int db = 0; db < DB; ++db)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    oacc[db][qb][v] *= alpha;
+            l_run[qb] += rs;
         }
-
-        // O^T += V^T P^T
+    };
+    auto o_phase = [&](const PFrag &pf, const char *slot, int cj, char *cslot, auto copies_c) __attribute__((always_inline)) {
+        constexpr bool copies = decltype(copies_c)::value;
         frag vf[2][DB];
-        read_v(slot, 0, vf[0]);
+        read_v(slot, std::integral_constant<int, 0>(), vf[0]);
         static_for<KS>([&](auto ks_c) __attribute__((always_inline)) {
             constexpr int ks = decltype(ks_c)::value;
             sync_nn_operands(vf[ks & 1]);
             if constexpr (ks + 1 < KS)
-                read_v(slot, ks + 1, vf[(ks + 1) & 1]);
+                read_v(slot, std::integral_constant<int, ks + 1>(), vf[(ks + 1) & 1]);
             constexpr int c0 = ks * Cfg::V_LOADS / KS, c1 = (ks + 1) * Cfg::V_LOADS / KS;
             if constexpr (copies && c1 > c0)
                 issue_v(cj, cslot, c0, c1);
@@ -287,6 +348,13 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
         });
         // every LDS read of this slot has returned
         wait_lds();
+    };
+    auto compute_tile = [&](int j, const char *slot, int cj, char *cslot, auto copies_c) __attribute__((always_inline)) {
+        SAcc sacc;
+        s_phase(sacc, slot, cj, cslot, copies_c);
+        PFrag pf;
+        softmax(sacc, pf, j);
+        o_phase(pf, slot, cj, cslot, copies_c);
     };
 
     auto pipeline = [&](auto stages_c) __attribute__((always_inline)) {

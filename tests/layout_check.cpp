@@ -278,6 +278,9 @@ void check_attn()
                 for (int l = 0; l < 64; ++l) {
                     const int off = v_tr_offset<D>(l, ks, dcol0, rr);
                     CHECK(off % 8 == 0 && off >= 0 && off + 8 <= BN * D * 2, "attn V: tr read offset %d", off);
+                    // the kernel puts the k-step's part in the read's offset field
+                    CHECK(off == v_tr_offset<D>(l, 0, dcol0, rr) + 32 * D * ks,
+                          "attn V: k-step %d does not move lane %d's read by 32 D ks bytes", ks, l);
                     word[l] = off / 4;
                     lk[l] = off / (D * 2);
                     ln[l] = (((off % (D * 2)) / 16) ^ nswz(lk[l])) * 8 + (off % 16) / 2;

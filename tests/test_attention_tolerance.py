@@ -1,9 +1,10 @@
 """The attention parity bound (tests/attn_error_model.py) checked on the CPU:
-it admits the kernel's arithmetic emulated in numpy (fp32 scores, fp32 exp2,
-P rounded to the input dtype for the second product, fp32 sums, the row sum
-of the unrounded values, output rounded), and it rejects the two plausible
-mistakes the GPU comparison must catch: one 64-key tile left out of the
-softmax, and the causal diagonal shifted by one key."""
+it admits the kernel's arithmetic emulated in numpy (key tiles of 128, fp32
+scores, a reference max per 32-query block that moves only when some query's
+max has grown by more than 2^8, fp32 exp2, P rounded to the input dtype for
+both the second product and the row sum, fp32 sums, output rounded), and it
+rejects the two plausible mistakes the GPU comparison must catch: one 64-key
+tile left out of the softmax, and the causal diagonal shifted by one key."""
 import numpy as np
 import pytest
 
@@ -17,20 +18,36 @@ F16, BF16 = inputs.F16, inputs.BF16
 NP16 = {F16: np.float16}
 
 
-def emulate_kernel(Q, K, V, dtype, causal):
+def emulate_kernel(Q, K, V, dtype, causal, bn=128, block=32):
     """fp32 emulation of the kernel's numerics for head (0, 0), all rows."""
     q = og.decode(Q[0, 0], dtype).astype(np.float32)
     k = og.decode(K[0, 0], dtype).astype(np.float32)
     v = og.decode(V[0, 0], dtype).astype(np.float32)
+    sq, skv = q.shape[0], k.shape[0]
     sl2 = np.float32(1.0 / np.sqrt(q.shape[1]) * 1.4426950408889634)
-    s = q @ k.T
-    if causal:
-        s = np.where(np.arange(k.shape[0])[None, :] <= np.arange(q.shape[0])[:, None], s, -np.inf).astype(np.float32)
-    m = s.max(axis=1, keepdims=True)
-    e = np.exp2(s * sl2 - m * sl2).astype(np.float32)
-    l = e.sum(axis=1, dtype=np.float32, keepdims=True)
-    p = og.decode(og.encode(e, dtype), dtype).astype(np.float32)     # P rounded to the input dtype
-    o = (p @ v) / l
+    m = np.full((sq, 1), -np.inf, np.float32)
+    l = np.zeros((sq, 1), np.float32)
+    acc = np.zeros((sq, v.shape[1]), np.float32)
+    with np.errstate(invalid="ignore"):
+        for k0 in range(0, skv, bn):
+            s = q @ k[k0:k0 + bn].T
+            if causal:
+                keys = np.arange(k0, min(k0 + bn, skv))
+                s = np.where(keys[None, :] <= np.arange(sq)[:, None], s, -np.inf).astype(np.float32)
+            mx = s.max(axis=1, keepdims=True)
+            for r0 in range(0, sq, block):
+                rr = slice(r0, r0 + block)
+                if ((mx[rr] - m[rr]) * sl2 > 8).any():
+                    m_new = np.maximum(m[rr], mx[rr])
+                    alpha = np.exp2((m[rr] - m_new) * sl2).astype(np.float32)
+                    l[rr] *= alpha
+                    acc[rr] *= alpha
+                    m[rr] = m_new
+            e = np.exp2(s * sl2 - m * sl2).astype(np.float32)
+            p = og.decode(og.encode(e, dtype), dtype).astype(np.float32)     # P rounded to the input dtype
+            l += p.sum(axis=1, dtype=np.float32, keepdims=True)
+            acc += p @ v[k0:k0 + bn]
+    o = acc / l
     return og.decode(og.encode(o.astype(np.float32), dtype), dtype).astype(np.float64)
 
 

@@ -1,9 +1,9 @@
 """GPU parity of the attention forward pass (the KV-length loop on the same
 pipelined LDS ring) against the float64 oracle, element by element, within
-the error bound of tests/attn_error_model.py: (2 u_in + u_out + 2 Skv u32 +
+the error bound of tests/attn_error_model.py: (3 u_in + u_out + 2 Skv u32 +
 2 D u32 A_i) sum_j P_ij |V_jd|, derived from the kernel's arithmetic (fp32
-scores and sums, P rounded to the input dtype for the second product, output
-rounded); a CPU test shows it rejects one dropped key tile and a shifted causal
+scores and sums, P rounded to the input dtype for the second product and the
+row sum, output rounded); a CPU test shows it rejects one dropped key tile and a shifted causal
 diagonal.  The result must not depend on the ring depth."""
 import numpy as np
 import pytest
