@@ -51,9 +51,14 @@ def emulate_kernel(Q, K, V, dtype, causal, bn=128, block=32):
     return og.decode(og.encode(o.astype(np.float32), dtype), dtype).astype(np.float64)
 
 
-def problem(dtype, causal, S=1024, nrows=None):
+def problem(dtype, causal, S=1024, nrows=None, grow=False):
     w = inputs.attention_custom(dtype, 1, 1, 1, S, S, 128, causal, seed=4242 + dtype + 2 * causal)
     Q, K, V = w.make()
+    if grow:
+        # key j scaled by 2^e_j, e_j rising from 0 to 6: the reference max moves on many tiles
+        e = (7 * np.arange(S)) // S
+        K = og.encode(og.decode(K, dtype).astype(np.float32) * np.exp2(e.astype(np.float32))[None, None, :, None],
+                      dtype)
     rows = np.arange(S if nrows is None else nrows)
     want = oatt.attention_rows(Q, K, V, dtype, 0, 0, rows, causal=causal)
     R, A = oatt.attention_rows_weights(Q, K, V, dtype, 0, 0, rows, causal=causal)
@@ -64,9 +69,10 @@ def rounded(x, dtype):
     return og.decode(og.encode(x.astype(np.float32), dtype), dtype).astype(np.float64)
 
 
+@pytest.mark.parametrize("grow", [False, True], ids=["normal", "growing_keys"])
 @pytest.mark.parametrize("dtype,causal", [(F16, False), (F16, True), (BF16, True)])
-def test_bound_admits_the_kernels_arithmetic(dtype, causal):
-    Q, K, V, want, R, A = problem(dtype, causal)
+def test_bound_admits_the_kernels_arithmetic(dtype, causal, grow):
+    Q, K, V, want, R, A = problem(dtype, causal, grow=grow)
     got = emulate_kernel(Q, K, V, dtype, causal)
     bad = em.violations(got, want, R, A, dtype, K.shape[2], 128)
     assert not bad.any(), "%d elements outside the bound" % int(bad.sum())

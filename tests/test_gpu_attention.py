@@ -122,3 +122,38 @@ def test_errors_leave_output_untouched():
         pg.attention(q[:, :2], k, k, out=out[:, :2].contiguous(), block_N=128, num_stages=3)
     torch.cuda.synchronize()
     assert bool((out == 5.0).all())
+
+
+def scaled_keys(K, dtype, profile):
+    """K with key j multiplied by 2^e_j (exact in the dtype): e_j rising from
+    0 to 6 over the sequence ("grow": the row max keeps moving, by less and by
+    more than 2^8 in the exponent from tile to tile) or falling from 6 to 0
+    ("shrink": the first tile holds the max)."""
+    S = K.shape[2]
+    e = (7 * np.arange(S)) // S
+    if profile == "shrink":
+        e = 6 - e
+    k = og.decode(K, dtype).astype(np.float32) * np.exp2(e.astype(np.float32))[None, None, :, None]
+    return og.encode(k, dtype)
+
+
+@pytest.mark.parametrize("profile", ["grow", "shrink"])
+@pytest.mark.parametrize("dtype,causal", [(F16, False), (F16, True), (BF16, False)])
+def test_reference_max_moves_across_tiles(profile, dtype, causal):
+    # key magnitudes change by powers of two along the sequence, so the
+    # softmax's reference max is moved (O and l rescaled) on some tiles and
+    # kept on others, with P up to 256
+    w = inputs.attention_custom(dtype, 1, 2, 1, 1024, 1024, 128, causal, seed=950 + dtype + 2 * causal)
+    Q, K, V = w.make()
+    K = scaled_keys(K, dtype, profile)
+    want = oatt.attention(Q, K, V, dtype, causal=causal)
+    R, A = weights(Q, K, V, dtype, causal)
+    first = None
+    for tile, s in (((256, 128, 512), 2), ((256, 64, 512), 4), ((128, 64, 256), 3)):
+        got = run(w, Q, K, V, tile, s)
+        assert_close(got, want, R, A, dtype, 1024, "%s tile %s S=%d" % (profile, tile, s))
+        if tile[1] == 64:
+            if first is None:
+                first = got
+            else:
+                assert np.array_equal(got, first), "the result depends on the workgroup shape at block_N 64"
