@@ -270,18 +270,22 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
         const int key0 = j * BN;
         if ((p.causal && key0 + BN - 1 > q0w) || key0 + BN > Skv) {
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+            for (int qb = 0; qb < QB; ++qb) {
+                // the last visible key, relative to this lane's first key of
+                // the tile: element v of block kb is key key0 + 4 lh + 32 kb +
+                // 8 (v / 4) + v % 4.  A score is kept by min(s, +inf) and masked
+                // by min(s, -inf), the infinity's sign taken from last - offset:
+                // no compares, branches or lane masks.
+                const int last = (p.causal ? min(q0w + 32 * qb + lr, Skv - 1) : Skv - 1) - key0 - 4 * lh;
 #pragma unroll
-                for (int qb = 0; qb < QB; ++qb)
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
-                        const int key = key0 + 32 * kb + 8 * (v >> 2) + 4 * lh + (v & 3);
-                        if ((p.causal && key > q0w + 32 * qb + lr) || key >= Skv)
-                            sacc[kb][qb][v] = -INFINITY;
-                        // one compare and select at a time, so the
-                        // scheduler does not hold every lane mask in SGPRs
-                        __builtin_amdgcn_sched_barrier(0);
+                        const int d = last - (32 * kb + 8 * (v >> 2) + (v & 3));
+                        const float lim = __builtin_bit_cast(float, ((unsigned)d & 0x80000000u) | 0x7f800000u);
+                        sacc[kb][qb][v] = fminf(sacc[kb][qb][v], lim);
                     }
+            }
         }
         // online softmax per query block (base-2 exponentials of
         // scale x log2(e) x score)
