@@ -157,3 +157,22 @@ def test_reference_max_moves_across_tiles(profile, dtype, causal):
                 first = got
             else:
                 assert np.array_equal(got, first), "the result depends on the workgroup shape at block_N 64"
+
+
+@pytest.mark.parametrize("tile", [(256, 128, 512), (256, 64, 256), (128, 64, 256)], ids=lambda t: "bm%d_bn%d_t%d" % t)
+def test_rows_past_sq_are_not_written(tile):
+    # O inside a larger buffer: 300 query rows per head is ragged against
+    # block_M, so the last query block has padding rows, whose stores must be
+    # dropped; the rows after the last head must keep their canary
+    w = inputs.attention_custom(F16, 1, 2, 1, 300, 300, 128, False, seed=990)
+    Q, K, V = w.make()
+    q, k, v = dev(Q, F16), dev(K, F16), dev(V, F16)
+    big = torch.full((2 * 300 + 512, 128), 7.0, dtype=torch.float16, device="cuda")
+    out = big[:600].view(1, 2, 300, 128)
+    bm, bn, th = tile
+    pg.attention(q, k, v, out=out, block_M=bm, block_N=bn, num_stages=2, threads=th)
+    torch.cuda.synchronize()
+    assert bool((big[600:] == 7.0).all()), "a store landed past the last query row"
+    want = oatt.attention(Q, K, V, F16)
+    R, A = weights(Q, K, V, F16, False)
+    assert_close(host(out), want, R, A, F16, 300, "tile %s" % (tile,))
