@@ -40,6 +40,8 @@ SWEEPS = [
     # the same 16 workgroups with 8 waves each (two per SIMD), at block_K 32 and 64
     ("cfg5b_longk_tile128x128x32_t512", "nt_f16_longk_512x512x65536", (128, 128, 32), 512, ("1", "2", "3", "4", "6")),
     ("cfg5b_longk_tile128x128x64_t512", "nt_f16_longk_512x512x65536", (128, 128, 64), 512, ("1", "2", "3", "4", "5")),
+    # the gfx950 default for this shape: twice the workgroups of the 128-wide tiles
+    ("cfg5b_longk_tile64x128x64_t256", "nt_f16_longk_512x512x65536", (64, 128, 64), 256, ("2", "3", "4", "6")),
     # one GPU's share of 4096^3 over 8 GPUs (512 x 4096 x 4096): 256, 128 or 32 workgroups
     ("shard8_tile64x128x64_t256", "nt_f16_shard8_512x4096x4096", (64, 128, 64), 256, ("2", "3", "4", "6")),
     ("shard8_tile128x128x64_t256", "nt_f16_shard8_512x4096x4096", (128, 128, 64), 256, ("2", "3", "4")),
