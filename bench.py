@@ -76,6 +76,9 @@ ATTENTION = [
     ("attn_f16_b4_h32_s4096_d128_causal", (256, 64, 512), (1, 2, 3, 4)),
     ("attn_f16_b4_h32_s4096_d128", (256, 128, 512), (1, 2)),
     ("attn_f16_b4_h32_s4096_d128_causal", (256, 128, 512), (1, 2)),
+    # the pages' fixed flashattn configuration: block_M 128, block_N 128, 2 stages, 256 threads
+    ("attn_f16_b4_h32_s4096_d128", (128, 128, 256), (1, 2)),
+    ("attn_f16_b4_h32_s4096_d128_causal", (128, 128, 256), (1, 2)),
     ("attn_f16_b4_h32_s4096_d128", (128, 64, 256), (1, 2, 3, 4)),
     ("attn_f16_b4_h32_s4096_d128", (256, 64, 256), (1, 2, 3, 4)),
     ("attn_f16_b4_h32_s4096_d128_causal", (256, 64, 256), (1, 2, 3, 4)),
