@@ -30,12 +30,14 @@ extern "C" {
  *
  *   Q          device pointer, [batch, heads, seq_q, dim], dtype elements, 16-byte aligned
  *   K, V       device pointers, [batch, kv_heads, seq_kv, dim], 16-byte aligned
- *   O          device pointer, [batch, heads, seq_q, dim], written in dtype, 16-byte aligned
+ *   O          device pointer, [batch, heads, seq_q, dim], written in dtype, 16-byte aligned;
+ *              nothing outside it is written (streaming stores)
  *   batch, heads, kv_heads, seq_q, seq_kv   >= 1; heads a multiple of kv_heads
  *              (query head h reads KV head h / (heads / kv_heads))
  *   dim        head dimension; 128 is built
  *   dtype      GEMM_F16 or GEMM_BF16 (pipegemm.h); fp32 scores, softmax and
- *              accumulation; P is rounded to dtype for the second product
+ *              accumulation; P is rounded to dtype for the second product and
+ *              for the row sum
  *   is_causal  1: query i sees keys j <= i (needs seq_q == seq_kv)
  *   scale      softmax scale: 0 selects 1 / sqrt(dim); otherwise it must be
  *              positive and finite (a negative, infinite or NaN scale is an
