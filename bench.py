@@ -82,6 +82,9 @@ ATTENTION = [
     ("attn_f16_b4_h32_s4096_d128", (128, 64, 256), (1, 2, 3, 4)),
     ("attn_f16_b4_h32_s4096_d128", (256, 64, 256), (1, 2, 3, 4)),
     ("attn_f16_b4_h32_s4096_d128_causal", (256, 64, 256), (1, 2, 3, 4)),
+    # bf16, causal, 32 query heads on 8 KV heads
+    ("attn_bf16_b2_h32_kv8_s2048_d128_causal", (256, 128, 512), (1, 2)),
+    ("attn_bf16_b2_h32_kv8_s2048_d128_causal", (256, 64, 512), (2, 3, 4)),
 ]
 PROFILES = os.path.join(ROOT, "profiles")
 
