@@ -12,7 +12,12 @@ stream), the shader clock the headline ran at with its MFMA utilisation at
 that clock, and the CPU oracle timed on a bounded row sample of the same GEMM
 together with the element-wise parity of the headline's C.
 
+The attention forward pass (the KV-length loop on the same ring) is swept
+per ring depth on its workloads and reported under "attention".
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-cpu-baseline]
+                       [--no-attention | --attention] [--no-clock] [--workload W --block BMxBNxBK
+                       --stages S[+A] --threads T] [--tune-tables] [--oracle-table]
 """
 import argparse
 import json
