@@ -90,6 +90,10 @@ ATTENTION = [
     # bf16, causal, 32 query heads on 8 KV heads
     ("attn_bf16_b2_h32_kv8_s2048_d128_causal", (256, 128, 512), (1, 2)),
     ("attn_bf16_b2_h32_kv8_s2048_d128_causal", (256, 64, 512), (2, 3, 4)),
+    # head dimension 64
+    ("attn_f16_b4_h32_s4096_d64", (256, 128, 512), (1, 2, 3, 4)),
+    ("attn_f16_b4_h32_s4096_d64", (256, 64, 512), (2, 3, 4)),
+    ("attn_f16_b4_h32_s4096_d64_causal", (256, 128, 512), (2, 3, 4)),
 ]
 PROFILES = os.path.join(ROOT, "profiles")
 

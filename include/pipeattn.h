@@ -34,7 +34,7 @@ extern "C" {
  *              nothing outside it is written (streaming stores)
  *   batch, heads, kv_heads, seq_q, seq_kv   >= 1; heads a multiple of kv_heads
  *              (query head h reads KV head h / (heads / kv_heads))
- *   dim        head dimension; 128 is built
+ *   dim        head dimension; 64 and 128 are built
  *   dtype      GEMM_F16 or GEMM_BF16 (pipegemm.h); fp32 scores, softmax and
  *              accumulation; P is rounded to dtype for the second product and
  *              for the row sum
@@ -43,8 +43,9 @@ extern "C" {
  *              positive and finite (a negative, infinite or NaN scale is an
  *              argument error, GEMM_ERR_ARG, reported before anything else)
  *   block_M    queries per workgroup, 32 or 64 per wave (threads = 2 x block_M
- *              or block_M); built: (block_M, block_N, threads) = (128, 64, 256),
- *              (256, 64, 512), (128, 128, 256), (256, 128, 512), (256, 64, 256)
+ *              or block_M); built, for each dim: (block_M, block_N, threads) =
+ *              (128, 64, 256), (256, 64, 512), (128, 128, 256), (256, 128, 512),
+ *              (256, 64, 256)
  *   block_N    keys per LDS tile: 64 or 128
  *   num_stages LDS ring slots, each holding one K and one V tile
  *              (num_stages x 2 x block_N x dim x 2 bytes of LDS); 1 = single

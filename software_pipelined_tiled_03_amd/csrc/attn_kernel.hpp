@@ -49,9 +49,9 @@ struct AttnArgs {
     int nq;            // ceil(Sq / BM)
 };
 
-template <int BN_, int WAVES_, int QB_ = 1>
+template <int BN_, int WAVES_, int QB_ = 1, int D_ = 128>
 struct AttnTile {
-    static constexpr int D = 128, BN = BN_, WAVES = WAVES_, QB = QB_, BM = 32 * QB * WAVES, THREADS = 64 * WAVES;
+    static constexpr int D = D_, BN = BN_, WAVES = WAVES_, QB = QB_, BM = 32 * QB * WAVES, THREADS = 64 * WAVES;
     static constexpr int K_BYTES = BN * D * 2, V_BYTES = BN * D * 2, SLOT_BYTES = K_BYTES + V_BYTES;
     static constexpr int K_LOADS = K_BYTES / (1024 * WAVES), V_LOADS = V_BYTES / (1024 * WAVES);
     static constexpr int LOADS = K_LOADS + V_LOADS;
@@ -60,6 +60,7 @@ struct AttnTile {
     static constexpr int DB = D / 32;   // 32-wide d blocks of O^T
     static constexpr int KS = BN / 16;  // 16-key steps of O^T
     static_assert(BN == 64 || BN == 128, "block_N must be 64 or 128");
+    static_assert(D == 64 || D == 128, "head dimension 64 or 128");
     static_assert(QB == 1 || QB == 2, "one or two 32-query blocks per wave");
     static_assert(K_BYTES % (1024 * WAVES) == 0 && K_LOADS >= 1, "whole 1 KiB copies per wave");
 };

@@ -9,10 +9,10 @@
 
 namespace pipegemm {
 
-template <class T, int BN, int WAVES, int QB>
+template <class T, int BN, int WAVES, int QB, int D>
 hipError_t attn_launch(const AttnArgs &args, int grid, int lds_bytes, hipStream_t stream)
 {
-    using Cfg = AttnTile<BN, WAVES, QB>;
+    using Cfg = AttnTile<BN, WAVES, QB, D>;
     static std::atomic<uint64_t> lds_set{0};
     const hipError_t attr_err = allow_full_lds((const void *)&attn_kernel<T, Cfg>, lds_set);
     if (attr_err != hipSuccess)
@@ -21,8 +21,8 @@ hipError_t attn_launch(const AttnArgs &args, int grid, int lds_bytes, hipStream_
     return hipGetLastError();
 }
 
-#define PG_ATTN_INSTANTIATE(BN, W, QB) \
-    template hipError_t attn_launch<PG_ELEM, BN, W, QB>(const AttnArgs &, int, int, hipStream_t);
+#define PG_ATTN_INSTANTIATE(BN, W, QB, D) \
+    template hipError_t attn_launch<PG_ELEM, BN, W, QB, D>(const AttnArgs &, int, int, hipStream_t);
 PG_ATTN_TILE_LIST(PG_ATTN_INSTANTIATE)
 #undef PG_ATTN_INSTANTIATE
 

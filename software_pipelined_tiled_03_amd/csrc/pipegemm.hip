@@ -332,14 +332,15 @@ double model_cost_us(const gemm_config &c, int64_t M, int64_t N, int64_t K)
 typedef hipError_t (*attn_launch_fn)(const AttnArgs &, int grid, int lds_bytes, hipStream_t);
 
 struct AttnInstance {
-    int dtype, bn, waves, qb;  // qb: 32-query blocks per wave
+    int dtype, bn, waves, qb, dim;  // qb: 32-query blocks per wave
     int loads_per_wave;  // 1 KiB copies per wave per K/V tile pair
     attn_launch_fn launch;
 };
 
-#define PG_ATTN_ROW(DT, T, BN, W, QB) {DT, BN, W, QB, 2 * BN * 128 * 2 / (1024 * W), &attn_launch<T, BN, W, QB>},
-#define PG_ATTN_ROW_F16(BN, W, QB) PG_ATTN_ROW(GEMM_F16, _Float16, BN, W, QB)
-#define PG_ATTN_ROW_BF16(BN, W, QB) PG_ATTN_ROW(GEMM_BF16, __bf16, BN, W, QB)
+#define PG_ATTN_ROW(DT, T, BN, W, QB, D) \
+    {DT, BN, W, QB, D, 2 * BN * D * 2 / (1024 * W), &attn_launch<T, BN, W, QB, D>},
+#define PG_ATTN_ROW_F16(BN, W, QB, D) PG_ATTN_ROW(GEMM_F16, _Float16, BN, W, QB, D)
+#define PG_ATTN_ROW_BF16(BN, W, QB, D) PG_ATTN_ROW(GEMM_BF16, __bf16, BN, W, QB, D)
 const AttnInstance kAttnInstances[] = {PG_ATTN_TILE_LIST(PG_ATTN_ROW_F16) PG_ATTN_TILE_LIST(PG_ATTN_ROW_BF16)};
 
 int64_t attn_lds_of(int bn, int dim, int stages)
@@ -383,8 +384,8 @@ int attn_validate(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Skv, in
     if (ptrs && ((((uintptr_t)ptrs[0]) | ((uintptr_t)ptrs[1]) | ((uintptr_t)ptrs[2]) | ((uintptr_t)ptrs[3])) & 15))
         return fail(GEMM_ERR_ALIGN, "Q, K, V and O must be 16-byte aligned");
     // (4) supported configuration and size limits
-    if (D != 128)
-        return fail(GEMM_ERR_UNSUPPORTED, "attention is built for dim 128 (got %lld)", (long long)D);
+    if (D != 64 && D != 128)
+        return fail(GEMM_ERR_UNSUPPORTED, "attention is built for dim 64 and 128 (got %lld)", (long long)D);
     // block_M = 32 x (query blocks per wave) x waves; threads 0 = one block per wave
     const int th = threads == 0 ? 2 * bm : threads;
     const int waves = th / 64;
@@ -394,12 +395,12 @@ int attn_validate(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Skv, in
     const int qb = bm / (32 * waves);
     const AttnInstance *in = nullptr;
     for (const AttnInstance &a : kAttnInstances)
-        if (a.dtype == dtype && a.bn == bn && a.waves == waves && a.qb == qb)
+        if (a.dtype == dtype && a.bn == bn && a.waves == waves && a.qb == qb && a.dim == D)
             in = &a;
     if (!in)
         return fail(GEMM_ERR_UNSUPPORTED, "no attention kernel built for block_M %d, block_N %d", bm, bn);
     const int s = stages < 1 ? 1 : stages;
-    if (s > kAttnMaxStages || (s - 1) * in->loads_per_wave > 63 || attn_lds_of(bn, 128, s) > 160 * 1024)
+    if (s > kAttnMaxStages || (s - 1) * in->loads_per_wave > 63 || attn_lds_of(bn, (int)D, s) > 160 * 1024)
         return fail(GEMM_ERR_UNSUPPORTED, "num_stages %d is not built for block_N %d with %d waves", s, bn,
                     th / 64);
     const int64_t lim = (int64_t)1 << 31;
@@ -458,7 +459,7 @@ int attn_fwd(const void *Q, const void *K, const void *V, void *O, int64_t batch
     a.stages = num_stages < 1 ? 1 : num_stages;
     a.nq = (int)((seq_q + block_M - 1) / block_M);
     const int grid = (int)(batch * heads * a.nq);
-    hipError_t e = in->launch(a, grid, (int)attn_lds_of(block_N, 128, a.stages), (hipStream_t)hip_stream);
+    hipError_t e = in->launch(a, grid, (int)attn_lds_of(block_N, (int)dim, a.stages), (hipStream_t)hip_stream);
     if (e != hipSuccess)
         return fail(GEMM_ERR_HIP, "attention launch failed: %s", hipGetErrorString(e));
     return ok();

@@ -108,18 +108,31 @@ PG_HD constexpr int nswz(int k)
 {
     return ((k & 3) << 2) | (((k >> 3) & 1) << 1);
 }
+// The same for rows of 64 elements (128 bytes, 8 chunks: the V tile of a
+// 64-dimension attention head).  Two rows share a 256-byte bank row, so rows
+// k and k+2 meet on the same banks; a transposed read's half-wave reads rows
+// k .. k+3 x 64 bytes at the same logical chunks, and flipping the chunk's
+// 64-byte half on every second pair of rows gives those 256 bytes 32
+// distinct 8-byte bank pairs.  Checked on the CPU.
+PG_HD constexpr int nswz64(int k) { return ((k >> 1) & 1) << 2; }
+template <int W>
+PG_HD constexpr int nswz_w(int k)
+{
+    static_assert(W == 64 || W >= 128, "N-contiguous rows of 64 or >= 128 elements");
+    return W == 64 ? nswz64(k) : nswz(k);
+}
 
 template <int BN>
 PG_HD constexpr int n_tile_offset(int k, int c)
 {
-    return (k * (BN / 8) + (c ^ nswz(k))) * 16;
+    return (k * (BN / 8) + (c ^ nswz_w<BN>(k))) * 16;
 }
 
 template <int BN>
 PG_HD constexpr void n_tile_unit(int u, int &k, int &c)
 {
     k = u / (BN / 8);
-    c = (u % (BN / 8)) ^ nswz(k);
+    c = (u % (BN / 8)) ^ nswz_w<BN>(k);
 }
 
 // Transposed read (ds_read_b64_tr_b16) feeding the 32x32x16 MFMA operand from
@@ -152,11 +165,12 @@ PG_HD constexpr int nn_tr_offset16(int lane, int kk, int ncol0, int h)
 }
 
 // ---------------------------------------------------------------------------
-// Attention tiles (head dimension D = 128).
+// Attention tiles (head dimension D = 64 or 128).
 //
-// The K tile (BN keys x D, D contiguous) is stored as two K-contiguous halves
-// of 64 columns, each laid out like a BK = 64 GEMM tile (so its operand reads
-// reuse the measured kswz<64> swizzle): half hf holds columns 64 hf .. +63.
+// The K tile (BN keys x D, D contiguous) is stored as K-contiguous halves of
+// 64 columns (one for D = 64, two for D = 128), each laid out like a BK = 64
+// GEMM tile (so its operand reads reuse the measured kswz<64> swizzle): half
+// hf holds columns 64 hf .. +63.
 template <int BN>
 PG_HD constexpr int attn_k_offset(int r, int c)  // c: 16-byte chunk 0..15 of row r
 {

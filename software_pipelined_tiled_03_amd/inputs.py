@@ -143,6 +143,10 @@ ATTENTION_WORKLOADS = {
                                                            4096, 4096, 128, True, 6100),
     "attn_bf16_b2_h32_kv8_s2048_d128_causal": AttentionWorkload("attn_bf16_b2_h32_kv8_s2048_d128_causal", BF16,
                                                                 2, 32, 8, 2048, 2048, 128, True, 6200),
+    "attn_f16_b4_h32_s4096_d64": AttentionWorkload("attn_f16_b4_h32_s4096_d64", F16, 4, 32, 32, 4096, 4096, 64,
+                                                   False, 6300),
+    "attn_f16_b4_h32_s4096_d64_causal": AttentionWorkload("attn_f16_b4_h32_s4096_d64_causal", F16, 4, 32, 32,
+                                                          4096, 4096, 64, True, 6400),
 }
 
 

@@ -256,20 +256,19 @@ void check_strip()
 // Attention tiles: the copies' destinations match the reads; the V^T
 // transposed reads deliver to lane l, slot j, the key attn_key_of_slot and
 // column dcol0 + l mod 32; the S^T accumulator holds P in that same key order.
-template <int BN>
+template <int BN, int D>
 void check_attn()
 {
-    constexpr int D = 128;
     // K: every copied unit is where the operand reads look for it
     std::set<int> seen;
-    for (int u = 0; u < BN * 16; ++u) {
+    for (int u = 0; u < BN * (D / 8); ++u) {
         int r = 0, c = 0;
         attn_k_unit<BN>(u, r, c);
-        CHECK(r >= 0 && r < BN && c >= 0 && c < 16, "attn K unit %d: (%d,%d) outside the tile", u, r, c);
+        CHECK(r >= 0 && r < BN && c >= 0 && c < D / 8, "attn K unit %d: (%d,%d) outside the tile", u, r, c);
         CHECK(attn_k_offset<BN>(r, c) == u * 16, "attn K unit %d: written (%d,%d) read elsewhere", u, r, c);
-        seen.insert(r * 16 + c);
+        seen.insert(r * (D / 8) + c);
     }
-    CHECK((int)seen.size() == BN * 16, "attn K: units do not cover the tile");
+    CHECK((int)seen.size() == BN * (D / 8), "attn K: units do not cover the tile");
     // V^T transposed reads
     for (int ks = 0; ks < BN / 16; ++ks)
         for (int dcol0 = 0; dcol0 < D; dcol0 += 32)
@@ -283,7 +282,7 @@ void check_attn()
                           "attn V: k-step %d does not move lane %d's read by 32 D ks bytes", ks, l);
                     word[l] = off / 4;
                     lk[l] = off / (D * 2);
-                    ln[l] = (((off % (D * 2)) / 16) ^ nswz(lk[l])) * 8 + (off % 16) / 2;
+                    ln[l] = (((off % (D * 2)) / 16) ^ nswz_w<D>(lk[l])) * 8 + (off % 16) / 2;
                 }
                 for (int l = 0; l < 64; ++l) {
                     const int G = l / 16, i = l % 16;
@@ -295,11 +294,13 @@ void check_attn()
                               n);
                     }
                 }
-                for (int g = 0; g < 64; g += 16) {
-                    std::set<int> quarters;
-                    for (int l = g; l < g + 16; ++l)
-                        quarters.insert((word[l] * 4 / 64) % 4);
-                    CHECK(quarters.size() == 4, "attn V ks=%d r=%d lanes %d..: rows share a bank quarter", ks, rr, g);
+                // each half-wave's 32 reads of 8 bytes hit 32 distinct 8-byte bank pairs
+                for (int g = 0; g < 64; g += 32) {
+                    std::set<int> pairs;
+                    for (int l = g; l < g + 32; ++l)
+                        pairs.insert((word[l] / 2) % 32);
+                    CHECK(pairs.size() == 32, "attn V D=%d ks=%d r=%d lanes %d..: %d of 32 bank pairs", D, ks, rr, g,
+                          (int)pairs.size());
                 }
             }
     // P: S^T accumulator element (kb, v) of lane l holds key 32 kb + 8 (v/4) + 4 (l/32) + v%4;
@@ -547,8 +548,10 @@ int main()
     check_strip<64>();
     check_strip<128>();
     check_ring();
-    check_attn<64>();
-    check_attn<128>();
+    check_attn<64, 128>();
+    check_attn<128, 128>();
+    check_attn<64, 64>();
+    check_attn<128, 64>();
     check_cbuf(1);
     check_cbuf(2);
     check_cbuf(4);

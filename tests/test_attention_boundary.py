@@ -57,7 +57,10 @@ def test_argument_errors():
 
 def test_alignment_and_unsupported():
     assert check(D=60) == pg.GEMM_ERR_ALIGN
-    assert check(D=64) == pg.GEMM_ERR_UNSUPPORTED
+    assert check(D=64) == pg.GEMM_OK                            # head dimensions 64 and 128 are built
+    assert check(D=64, bm=256, th=256) == pg.GEMM_OK            # two blocks per wave at 64 too
+    assert check(D=96) == pg.GEMM_ERR_UNSUPPORTED
+    assert check(D=256, bn=64, s=1) == pg.GEMM_ERR_UNSUPPORTED  # fits the budget, not built
     assert check(bm=128, th=512) == pg.GEMM_ERR_UNSUPPORTED     # threads must be 2 x block_M
     assert check(bm=256, th=256, bn=128) == pg.GEMM_ERR_UNSUPPORTED   # not built (two blocks per wave, 128 keys)
     assert check(bm=256, th=512, bn=128) == pg.GEMM_OK

@@ -176,3 +176,24 @@ def test_rows_past_sq_are_not_written(tile):
     want = oatt.attention(Q, K, V, F16)
     R, A = weights(Q, K, V, F16, False)
     assert_close(host(out), want, R, A, F16, 300, "tile %s" % (tile,))
+
+
+@pytest.mark.parametrize("tile", TILES, ids=lambda t: "bm%d_bn%d_t%d" % t)
+@pytest.mark.parametrize("dtype,causal", [(F16, True), (BF16, False)])
+def test_head_dim_64_every_tile_every_depth(tile, dtype, causal):
+    # D = 64: one K half, V rows of 128 bytes with their own swizzle; ragged
+    # lengths, 4 query heads on 2 KV heads
+    w = inputs.attention_custom(dtype, 2, 4, 2, 300, 300, 64, causal, seed=1300 + dtype + 2 * causal + tile[1])
+    Q, K, V = w.make()
+    want = oatt.attention(Q, K, V, dtype, causal=causal)
+    R, A = weights(Q, K, V, dtype, causal)
+    first = None
+    for s in (1, 2, 3, 4):
+        if pg.attn_check(2, 4, 2, 300, 300, 64, dtype, int(causal), tile[0], tile[1], s, tile[2], 160 * 1024):
+            continue
+        got = run(w, Q, K, V, tile, s)
+        assert_close(got, want, R, A, dtype, 300, "D=64 tile %s S=%d" % (tile, s))
+        if first is None:
+            first = got
+        else:
+            assert np.array_equal(got, first), "ring depth %d changed the result" % s
