@@ -94,6 +94,10 @@ ATTENTION = [
     ("attn_f16_b4_h32_s4096_d64", (256, 128, 512), (1, 2, 3, 4)),
     ("attn_f16_b4_h32_s4096_d64", (256, 64, 512), (2, 3, 4)),
     ("attn_f16_b4_h32_s4096_d64_causal", (256, 128, 512), (2, 3, 4)),
+    # two 32-query blocks per wave, 8 waves (fits the registers at D = 64)
+    ("attn_f16_b4_h32_s4096_d64", (512, 64, 512), (2, 3, 4)),
+    ("attn_f16_b4_h32_s4096_d64", (512, 128, 512), (2,)),
+    ("attn_f16_b4_h32_s4096_d64_causal", (512, 64, 512), (2, 3, 4)),
 ]
 PROFILES = os.path.join(ROOT, "profiles")
 

@@ -45,7 +45,7 @@ extern "C" {
  *   block_M    queries per workgroup, 32 or 64 per wave (threads = 2 x block_M
  *              or block_M); built, for each dim: (block_M, block_N, threads) =
  *              (128, 64, 256), (256, 64, 512), (128, 128, 256), (256, 128, 512),
- *              (256, 64, 256)
+ *              (256, 64, 256); for dim 64 also (512, 64, 512), (512, 128, 512)
  *   block_N    keys per LDS tile: 64 or 128
  *   num_stages LDS ring slots, each holding one K and one V tile
  *              (num_stages x 2 x block_N x dim x 2 bytes of LDS); 1 = single

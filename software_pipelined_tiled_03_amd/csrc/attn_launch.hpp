@@ -26,6 +26,8 @@ constexpr int kAttnMaxStages = 4;
     X(64, 8, 1, 64)          \
     X(128, 4, 1, 64)         \
     X(128, 8, 1, 64)         \
-    X(64, 4, 2, 64)
+    X(64, 4, 2, 64)          \
+    X(64, 8, 2, 64)          \
+    X(128, 8, 2, 64)
 
 }  // namespace pipegemm

@@ -178,7 +178,11 @@ def test_rows_past_sq_are_not_written(tile):
     assert_close(host(out), want, R, A, F16, 300, "tile %s" % (tile,))
 
 
-@pytest.mark.parametrize("tile", TILES, ids=lambda t: "bm%d_bn%d_t%d" % t)
+# at D = 64 two 32-query blocks per wave also fit with two waves per SIMD
+TILES_D64 = TILES + [(512, 64, 512), (512, 128, 512)]
+
+
+@pytest.mark.parametrize("tile", TILES_D64, ids=lambda t: "bm%d_bn%d_t%d" % t)
 @pytest.mark.parametrize("dtype,causal", [(F16, True), (BF16, False)])
 def test_head_dim_64_every_tile_every_depth(tile, dtype, causal):
     # D = 64: one K half, V rows of 128 bytes with their own swizzle; ragged
