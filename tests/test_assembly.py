@@ -256,3 +256,48 @@ def test_knee_register_table_matches_the_builds(nt_f16_asm, nn_bf16_asm):
         # the occupancy the table implies is the same for every build of the tile
         for regs in (nt[key], nn[key]):
             assert 512 // (-(-regs // 8) * 8) == knee.reg_waves_per_simd(*key), key
+
+
+@pytest.fixture(scope="module")
+def attn_f16_asm(tmp_path_factory):
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("asm") / "attn_f16.s"
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+                    "-packed-fp32-ops", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC, "-DPG_ELEM=_Float16",
+                    "--cuda-device-only", "-S", os.path.join(CSRC, "attn_kernels.hip"), "-o", str(out)], check=True,
+                   capture_output=True)
+    return out.read_text()
+
+
+def _scratch_in_loops(text):
+    """(kernel, line) of every scratch (spill) access inside a loop: the
+    compiler marks each basic block of a loop with 'Loop Header' or 'in
+    Loop' on its label line."""
+    found = []
+    kernel, in_loop = None, False
+    for line in text.splitlines():
+        if re.match(r"^_ZN8pipegemm\w+:", line):
+            kernel, in_loop = line.split(":")[0], False
+        elif re.match(r"^(\.LBB\w+:|; %bb\.\d+:)", line):
+            in_loop = "Loop Header" in line or "in Loop" in line
+        elif in_loop and "scratch_" in line and kernel:
+            found.append((kernel, line.strip()))
+    return found
+
+
+def test_no_spill_traffic_inside_any_loop(nt_f16_asm, nn_bf16_asm, attn_f16_asm):
+    # register spills, where the compiler needs them at all (the 4-wave
+    # 256x256 tiles hold 512 registers), stay outside the K and KV loops
+    for text in (nt_f16_asm, nn_bf16_asm, attn_f16_asm):
+        assert text.count("Loop Header") > 0
+        bad = _scratch_in_loops(text)
+        assert not bad, bad[:3]
+
+
+def test_attention_and_headline_kernels_do_not_spill(nt_f16_asm, attn_f16_asm):
+    for m in re.finditer(r"\.name:\s+(\S+)\s.*?\.vgpr_spill_count:\s+(\d+)", attn_f16_asm, re.S):
+        assert int(m.group(2)) == 0, m.group(1)
+    for m in re.finditer(r"\.name:\s+(\S+)\s.*?\.vgpr_spill_count:\s+(\d+)", nt_f16_asm, re.S):
+        if m.group(1) == HEADLINE:
+            assert int(m.group(2)) == 0
