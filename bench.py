@@ -120,6 +120,23 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
+ATTN_SOURCES = ("attn_kernel.hpp", "attn_kernels.hip", "attn_launch.hpp", "pipegemm_kernel.hpp", "pipegemm_layout.hpp")
+
+
+def attention_source_hash():
+    """sha256 over the contents, in this order, of the device-code sources
+    the attention kernel is built from (its own files and the GEMM headers it
+    takes the ring and layouts from)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "software_pipelined_tiled_03_amd", "csrc")
+    for name in ATTN_SOURCES:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def measured_traffic(block, stages, a_lead, threads):
     """HBM bytes per launch from a committed rocprofv3 summary of this exact
     kernel configuration, or None if there is none or the kernel sources

@@ -70,6 +70,24 @@ def test_profiled_traffic_is_used_only_for_the_profiled_sources(monkeypatch):
     assert int(fields["hbm_bytes_per_launch"]) >= 2 * 3 * 4096 * 4096
 
 
+def _profile_hash(name):
+    for line in open(os.path.join(bench.PROFILES, name)):
+        if line.startswith("- source_sha256"):
+            return line.split(":", 1)[1].strip()
+    raise AssertionError("%s carries no source_sha256 line" % name)
+
+
+@pytest.mark.parametrize("name", ["gemm_nt_f16_4096_256x256x64_s2a_t512.md", "stage_sweep_4096.md",
+                                  "stage_sweep_small_ragged_longk.md"])
+def test_committed_gemm_profiles_match_the_kernel_sources(name):
+    # a kernel change must come with new profiles, or the bench line's traffic goes null
+    assert _profile_hash(name) == bench.kernel_source_hash(), "%s was taken from other kernel sources" % name
+
+
+def test_committed_attention_profile_matches_the_kernel_sources():
+    assert _profile_hash("attention_fwd_sweep.md") == bench.attention_source_hash()
+
+
 def test_shape_ceiling_counts_rounds_of_the_compute_units():
     # 4096^3 at 256 x 256: 256 tiles, one round, no padding
     assert bench.shape_ceiling(4096, 4096, 4096, (256, 256, 64)) == pytest.approx(bench.PEAK_TFLOPS)
