@@ -81,6 +81,15 @@ __device__ __forceinline__ i16x4 ds_read_tr16_b64_at(const char *addr)
     return v;
 }
 
+// s_waitcnt lgkmcnt(N): all but the N most recent LDS reads of this wave
+// have returned (LDS reads return in issue order).
+template <int N>
+__device__ __forceinline__ void wait_lds_keep()
+{
+    static_assert(N >= 0 && N < 16, "lgkmcnt is 4 bits");
+    __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (N << 8));
+}
+
 // c + a + b with a, b in the input dtype (v_dot2c_f32_{f16,bf16} against
 // (1, 1): exact products, fp32 accumulation)
 __device__ __forceinline__ float dot2_ones(_Float16 a, _Float16 b, float c)
@@ -335,13 +344,24 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
     };
     auto o_phase = [&](const PFrag &pf, const char *slot, int cj, char *cslot, auto copies_c) __attribute__((always_inline)) {
         constexpr bool copies = decltype(copies_c)::value;
-        frag vf[2][DB];
+        // V^T fragments are read two k-steps ahead (three buffers): the wait
+        // before step ks lets the 2 DB transposed reads of step ks + 1 stay in
+        // flight, and LDS reads return in issue order.
+        frag vf[3][DB];
         read_v(slot, std::integral_constant<int, 0>(), vf[0]);
+        read_v(slot, std::integral_constant<int, 1>(), vf[1]);
         static_for<KS>([&](auto ks_c) __attribute__((always_inline)) {
             constexpr int ks = decltype(ks_c)::value;
-            sync_nn_operands(vf[ks & 1]);
-            if constexpr (ks + 1 < KS)
-                read_v(slot, std::integral_constant<int, ks + 1>(), vf[(ks + 1) & 1]);
+            if constexpr (ks + 1 < KS) {
+                wait_lds_keep<2 * DB>();
+#pragma unroll
+                for (int g = 0; g < DB; ++g)
+                    asm volatile("" : "+v"(vf[ks % 3][g]));
+            } else {
+                sync_nn_operands(vf[ks % 3]);
+            }
+            if constexpr (ks + 2 < KS)
+                read_v(slot, std::integral_constant<int, ks + 2>(), vf[(ks + 2) % 3]);
             constexpr int c0 = ks * Cfg::V_LOADS / KS, c1 = (ks + 1) * Cfg::V_LOADS / KS;
             if constexpr (copies && c1 > c0)
                 issue_v(cj, cslot, c0, c1);
@@ -349,7 +369,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
             for (int db = 0; db < DB; ++db)
 #pragma unroll
                 for (int qb = 0; qb < QB; ++qb)
-                    oacc[db][qb] = E::mfma(vf[ks & 1][db], pf[ks][qb], oacc[db][qb]);
+                    oacc[db][qb] = E::mfma(vf[ks % 3][db], pf[ks][qb], oacc[db][qb]);
         });
         // every LDS read of this slot has returned
         wait_lds();
