@@ -285,7 +285,10 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
                 // the tile: element v of block kb is key key0 + 4 lh + 32 kb +
                 // 8 (v / 4) + v % 4.  A score is kept by min(s, +inf) and masked
                 // by min(s, -inf), the infinity's sign taken from last - offset:
-                // no compares, branches or lane masks.
+                // no compares, branches or lane masks.  The IEEE 754-2019
+                // minimum (v_minimum_f32) needs no quieting of its inputs,
+                // which the IEEE-mode minNum would spend two instructions on
+                // per score; the scores and the infinities are never NaN.
                 const int last = (p.causal ? min(q0w + 32 * qb + lr, Skv - 1) : Skv - 1) - key0 - 4 * lh;
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
@@ -293,7 +296,7 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
                     for (int v = 0; v < 16; ++v) {
                         const int d = last - (32 * kb + 8 * (v >> 2) + (v & 3));
                         const float lim = __builtin_bit_cast(float, ((unsigned)d & 0x80000000u) | 0x7f800000u);
-                        sacc[kb][qb][v] = fminf(sacc[kb][qb][v], lim);
+                        sacc[kb][qb][v] = __builtin_elementwise_minimum(sacc[kb][qb][v], lim);
                     }
             }
         }
