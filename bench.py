@@ -120,7 +120,8 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
-ATTN_SOURCES = ("attn_kernel.hpp", "attn_kernels.hip", "attn_launch.hpp", "pipegemm_kernel.hpp", "pipegemm_layout.hpp")
+ATTN_SOURCES = ("attn_kernel.hpp", "attn_kernels.hip", "attn_launch.hpp", "attn_map.hpp", "pipegemm_kernel.hpp",
+                "pipegemm_layout.hpp")
 
 
 def attention_source_hash():

@@ -31,6 +31,7 @@
 
 #include <math.h>
 
+#include "attn_map.hpp"
 #include "pipegemm_kernel.hpp"
 
 namespace pipegemm {
@@ -117,11 +118,10 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lr = lane & 31, lh = lane >> 5;
 
-    // Work item: the last query blocks first (with a causal mask they have the
-    // most key tiles), then (batch, head).
-    const int bhs = p.B * p.H;
-    const int qblk = p.nq - 1 - (int)blockIdx.x / bhs;
-    const int bh = (int)blockIdx.x % bhs;
+    // Work item (attn_work_item): longest query blocks first with the causal
+    // mask, a head's blocks together on one XCD without it.
+    int bh, qblk;
+    attn_work_item((int)blockIdx.x, p.B * p.H, p.nq, p.causal != 0, bh, qblk);
     const int b = bh / p.H, h = bh % p.H;
     const int hk = h / p.groups;
     const int q0 = qblk * BM;

@@ -14,6 +14,7 @@
 #include <algorithm>
 
 #include "pipegemm_layout.hpp"
+#include "attn_map.hpp"
 
 using namespace pipegemm;
 
@@ -516,6 +517,46 @@ void check_map_tile()
     }
 }
 
+// Attention work items: every (head row, query block) goes to exactly one
+// workgroup, with and without the mask.  Causal: the first B H ids take the
+// last query block of every head.  Without the mask, when B H is a multiple
+// of 8, all blocks of a head land on one XCD (id mod 8), e.g. 16 whole heads
+// per XCD at 4 x 32 heads and 16 query blocks.
+void check_attn_map()
+{
+    std::vector<int> seen;
+    for (int bhs = 1; bhs <= 48; ++bhs)
+        for (int nq = 1; nq <= 40; ++nq)
+            for (int causal = 0; causal < 2; ++causal) {
+                seen.assign(bhs * nq, 0);
+                for (int bid = 0; bid < bhs * nq; ++bid) {
+                    int bh = -1, qb = -1;
+                    attn_work_item(bid, bhs, nq, causal != 0, bh, qb);
+                    if (bh < 0 || bh >= bhs || qb < 0 || qb >= nq) {
+                        CHECK(false, "attn_work_item(%d, %d, %d, %d) -> (%d,%d) outside", bid, bhs, nq, causal, bh, qb);
+                        continue;
+                    }
+                    ++seen[bh * nq + qb];
+                    if (causal && bid < bhs)
+                        CHECK(qb == nq - 1, "causal id %d of %d x %d does not take a last query block", bid, bhs, nq);
+                }
+                for (int t = 0; t < bhs * nq; ++t)
+                    CHECK(seen[t] == 1, "attn work item (%d,%d) of %d x %d (causal %d) owned by %d workgroups",
+                          t / nq, t % nq, bhs, nq, causal, seen[t]);
+                if (!causal && bhs % 8 == 0)
+                    for (int bh = 0; bh < bhs; ++bh) {
+                        std::set<int> xcds;
+                        for (int bid = 0; bid < bhs * nq; ++bid) {
+                            int b2 = 0, q2 = 0;
+                            attn_work_item(bid, bhs, nq, false, b2, q2);
+                            if (b2 == bh)
+                                xcds.insert(bid % 8);
+                        }
+                        CHECK(xcds.size() == 1, "head row %d of %d x %d spans %zu XCDs", bh, bhs, nq, xcds.size());
+                    }
+            }
+}
+
 // Epilogue batches: a divisor of FM that fits, and the largest such.
 void check_epi_batch()
 {
@@ -532,6 +573,7 @@ void check_epi_batch()
 int main()
 {
     check_map_tile();
+    check_attn_map();
     check_epi_batch();
     check_k_tile<32>(256);
     check_k_tile<64>(256);
