@@ -201,3 +201,22 @@ def test_head_dim_64_every_tile_every_depth(tile, dtype, causal):
             first = got
         else:
             assert np.array_equal(got, first), "ring depth %d changed the result" % s
+
+
+@pytest.mark.parametrize("B,H,Hkv", [(3, 6, 3), (1, 5, 5), (2, 12, 4)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_every_work_item_once(B, H, Hkv, causal):
+    # head counts that are not multiples of the 8 XCDs, query heads sharing KV
+    # heads, and several query blocks per head: every (head, query block) must
+    # be computed by exactly one workgroup in both work orders, so O starts as
+    # NaN and every element must come out finite and inside the bound
+    w = inputs.attention_custom(F16, B, H, Hkv, 700, 700, 128, causal, seed=1300 + 7 * B + H + causal)
+    Q, K, V = w.make()
+    want = oatt.attention(Q, K, V, F16, causal=causal)
+    R, A = weights(Q, K, V, F16, causal)
+    for bm, bn, th in [(256, 128, 512), (256, 64, 512)]:
+        O = torch.full((B, H, 700, 128), float("nan"), dtype=torch.float16, device="cuda")
+        pg.attention(dev(Q, F16), dev(K, F16), dev(V, F16), causal=causal, out=O, block_M=bm, block_N=bn,
+                     num_stages=2, threads=th)
+        torch.cuda.synchronize()
+        assert_close(host(O), want, R, A, F16, 700, "B=%d H=%d Hkv=%d tile %d x %d" % (B, H, Hkv, bm, bn))
