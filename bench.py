@@ -127,14 +127,18 @@ ATTN_SOURCES = ("attn_kernel.hpp", "attn_kernels.hip", "attn_launch.hpp", "attn_
 def attention_source_hash():
     """sha256 over the contents, in this order, of the device-code sources
     the attention kernel is built from (its own files and the GEMM headers it
-    takes the ring and layouts from)."""
+    takes the ring and layouts from), then the compiler flags only its units
+    get (build.ATTN_FLAGS)."""
     import hashlib
+
+    from software_pipelined_tiled_03_amd import build
 
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "software_pipelined_tiled_03_amd", "csrc")
     for name in ATTN_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
+    h.update(" ".join(build.ATTN_FLAGS).encode())
     return h.hexdigest()
 
 

@@ -263,8 +263,11 @@ def attn_f16_asm(tmp_path_factory):
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not available")
     out = tmp_path_factory.mktemp("asm") / "attn_f16.s"
+    from software_pipelined_tiled_03_amd import build
+
     subprocess.run([HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-                    "-packed-fp32-ops", "-I" + os.path.join(ROOT, "include"), "-I" + CSRC, "-DPG_ELEM=_Float16",
+                    "-packed-fp32-ops", *build.ATTN_FLAGS, "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
+                    "-DPG_ELEM=_Float16",
                     "--cuda-device-only", "-S", os.path.join(CSRC, "attn_kernels.hip"), "-o", str(out)], check=True,
                    capture_output=True)
     return out.read_text()
@@ -301,3 +304,21 @@ def test_attention_and_headline_kernels_do_not_spill(nt_f16_asm, attn_f16_asm):
     for m in re.finditer(r"\.name:\s+(\S+)\s.*?\.vgpr_spill_count:\s+(\d+)", nt_f16_asm, re.S):
         if m.group(1) == HEADLINE:
             assert int(m.group(2)) == 0
+
+
+def test_one_wave_per_simd_attention_tiles_move_no_accumulators(attn_f16_asm):
+    # built with the VGPR form of the MFMAs (build.ATTN_FLAGS), the attention
+    # tiles keep their accumulators in VGPRs: no v_accvgpr copies between the
+    # register files (by default the 4-wave tiles made 1000-3400 per kernel),
+    # except the two-block D = 128 tile, whose 300-odd registers exceed 256
+    seen = 0
+    for m in re.finditer(r"^(_ZN8pipegemm11attn_kernel\w+):[^\n]*\n(.*?)\.Lfunc_end", attn_f16_asm, re.S | re.M):
+        name, body = m.group(1), m.group(2)
+        tile = re.search(r"AttnTileILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E", name).groups()
+        moves = body.count("v_accvgpr_read") + body.count("v_accvgpr_write")
+        seen += 1
+        if tile == ("64", "4", "2", "128"):
+            assert moves < 500, (tile, moves)
+        else:
+            assert moves == 0, (tile, moves)
+    assert seen == 12
