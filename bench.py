@@ -84,7 +84,9 @@ ATTENTION = [
     # the pages' fixed flashattn configuration: block_M 128, block_N 128, 2 stages, 256 threads
     ("attn_f16_b4_h32_s4096_d128", (128, 128, 256), (1, 2)),
     ("attn_f16_b4_h32_s4096_d128_causal", (128, 128, 256), (1, 2)),
+    # 4 waves: two workgroups share a compute unit where the ring fits in half the LDS
     ("attn_f16_b4_h32_s4096_d128", (128, 64, 256), (1, 2, 3, 4)),
+    ("attn_f16_b4_h32_s4096_d128_causal", (128, 64, 256), (1, 2)),
     ("attn_f16_b4_h32_s4096_d128", (256, 64, 256), (1, 2, 3, 4)),
     ("attn_f16_b4_h32_s4096_d128_causal", (256, 64, 256), (1, 2, 3, 4)),
     # bf16, causal, 32 query heads on 8 KV heads
@@ -98,6 +100,9 @@ ATTENTION = [
     ("attn_f16_b4_h32_s4096_d64", (512, 64, 512), (2, 3, 4)),
     ("attn_f16_b4_h32_s4096_d64", (512, 128, 512), (2,)),
     ("attn_f16_b4_h32_s4096_d64_causal", (512, 64, 512), (2, 3, 4)),
+    # 4 waves at D = 64
+    ("attn_f16_b4_h32_s4096_d64", (128, 64, 256), (1, 2, 3)),
+    ("attn_f16_b4_h32_s4096_d64_causal", (128, 64, 256), (1, 2, 3)),
 ]
 PROFILES = os.path.join(ROOT, "profiles")
 
