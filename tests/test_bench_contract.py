@@ -50,6 +50,21 @@ def test_every_sweep_point_is_a_valid_configuration():
             assert st == 0, (label, d, st)
 
 
+def test_every_attention_point_is_a_valid_configuration():
+    import software_pipelined_tiled_03_amd as pg
+    from software_pipelined_tiled_03_amd import inputs
+
+    seen = set()
+    for name, (bm, bn, th), depths in bench.ATTENTION:
+        w = inputs.attention_workload(name)
+        for s in depths:
+            st = pg.attn_check(w.batch, w.heads, w.kv_heads, w.seq_q, w.seq_kv, w.dim, w.dtype, int(w.causal), bm, bn,
+                               s, th, 163840)
+            assert st == 0, (name, bm, bn, th, s, st, pg.last_error())
+            assert (name, bm, bn, th, s) not in seen, "timed twice: %s" % ((name, bm, bn, th, s),)
+            seen.add((name, bm, bn, th, s))
+
+
 def test_profiled_traffic_is_used_only_for_the_profiled_sources(monkeypatch):
     h = bench.HEADLINE
     args = (h["block"], h["num_stages"], h["a_lead"], h["threads"])
