@@ -403,10 +403,14 @@ int attn_validate(int64_t B, int64_t H, int64_t Hkv, int64_t Sq, int64_t Skv, in
     if (s > kAttnMaxStages || (s - 1) * in->loads_per_wave > 63 || attn_lds_of(bn, (int)D, s) > 160 * 1024)
         return fail(GEMM_ERR_UNSUPPORTED, "num_stages %d is not built for block_N %d with %d waves", s, bn,
                     th / 64);
+    // the limits are checked by division (for positive x, y: x y >= lim
+    // exactly when x > (lim - 1) / y), so that no product of the sizes can
+    // overflow whatever the caller passes
     const int64_t lim = (int64_t)1 << 31;
-    if (Sq * D * 2 >= lim || Skv * D * 2 >= lim)
+    if (Sq > (lim - 1) / (D * 2) || Skv > (lim - 1) / (D * 2))
         return fail(GEMM_ERR_UNSUPPORTED, "one head's sequence must be below 2 GiB");
-    if (B * H * ((Sq + bm - 1) / bm) >= lim || B * H >= lim)
+    const int64_t nq = Sq / bm + (Sq % bm != 0);
+    if (B > (lim - 1) / H || B * H > (lim - 1) / nq)
         return fail(GEMM_ERR_UNSUPPORTED, "too many workgroups");
     if (inst)
         *inst = in;

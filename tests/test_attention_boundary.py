@@ -76,6 +76,21 @@ def test_grouped_and_causal_configurations_are_valid():
     assert check(Sq=300, Skv=777) == pg.GEMM_OK
 
 
+def test_sizes_past_the_limits_are_rejected_without_overflow():
+    # products of these sizes overflow 64 bits: the limits are checked by division
+    big = 1 << 61
+    assert check(Sq=big, Skv=big, causal=1) == pg.GEMM_ERR_UNSUPPORTED
+    assert "2 GiB" in pg.last_error()
+    assert check(B=1 << 40, H=1 << 40, Hkv=1) == pg.GEMM_ERR_UNSUPPORTED
+    assert "workgroups" in pg.last_error()
+    # just inside and just past one head's 2 GiB of Q at dim 128 (256-byte rows)
+    assert check(Sq=(1 << 23) - 1, Skv=64) == pg.GEMM_OK
+    assert check(Sq=1 << 23, Skv=64) == pg.GEMM_ERR_UNSUPPORTED
+    # workgroups: B H ceil(Sq / block_M) must stay below 2^31
+    assert check(B=1 << 16, H=1 << 15, Hkv=1 << 15, Sq=128, Skv=64, bm=128) == pg.GEMM_ERR_UNSUPPORTED
+    assert check(B=1 << 15, H=(1 << 16) - 1, Hkv=(1 << 16) - 1, Sq=128, Skv=64, bm=128) == pg.GEMM_OK
+
+
 def test_scale_must_be_zero_or_positive_and_finite():
     # rejected as an argument error before any device is touched: the
     # pointers below are aligned placeholders that are never dereferenced
