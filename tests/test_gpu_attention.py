@@ -203,11 +203,12 @@ def test_head_dim_64_every_tile_every_depth(tile, dtype, causal):
             assert np.array_equal(got, first), "ring depth %d changed the result" % s
 
 
-@pytest.mark.parametrize("B,H,Hkv", [(3, 6, 3), (1, 5, 5), (2, 12, 4)])
+@pytest.mark.parametrize("B,H,Hkv", [(3, 6, 3), (1, 5, 5), (2, 12, 4), (2, 8, 1)])
 @pytest.mark.parametrize("causal", [False, True])
 def test_every_work_item_once(B, H, Hkv, causal):
     # head counts that are not multiples of the 8 XCDs, query heads sharing KV
-    # heads, and several query blocks per head: every (head, query block) must
+    # heads (all of them one KV head in the last case), and several query
+    # blocks per head: every (head, query block) must
     # be computed by exactly one workgroup in both work orders, so O starts as
     # NaN and every element must come out finite and inside the bound
     w = inputs.attention_custom(F16, B, H, Hkv, 700, 700, 128, causal, seed=1300 + 7 * B + H + causal)
