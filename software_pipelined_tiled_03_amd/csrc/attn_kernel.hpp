@@ -385,16 +385,33 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
         o_phase(pf, slot, cj, cslot, copies_c);
     };
 
+    // With the causal mask the tiles whose first key lies past this wave's
+    // last query are the workgroup's last ones, and the wave has nothing to
+    // add in them: every score is masked, P is zero, and m, l and O stay as
+    // they are, bit for bit.  The wave computes only the tiles before them
+    // (nt_w); in the rest it issues its share of the copies and passes the
+    // same waits and barriers as the other waves, whose SIMD partner then has
+    // the matrix core to itself.  Not on the two-block 128-key 8-wave tile,
+    // which is at 256 registers and would spill.
+    constexpr bool kSkipIdle = !(WAVES == 8 && QB == 2 && BN == 128);
+    const int nt_w = (kSkipIdle && p.causal) ? min(nt, (q0w + 32 * QB - 1) / BN + 1) : nt;
     auto pipeline = [&](auto stages_c) __attribute__((always_inline)) {
         constexpr int S = decltype(stages_c)::value;
         constexpr int L = Cfg::LOADS;
         if constexpr (S == 1) {
-            for (int j = 0; j < nt; ++j) {
+            for (int j = 0; j < nt_w; ++j) {
                 issue_k(j, smem, 0, Cfg::K_LOADS);
                 issue_v(j, smem, 0, Cfg::V_LOADS);
                 wait_vmcnt<0>();
                 barrier();
                 compute_tile(j, smem, 0, smem, std::false_type());
+                barrier();
+            }
+            for (int j = nt_w; j < nt; ++j) {
+                issue_k(j, smem, 0, Cfg::K_LOADS);
+                issue_v(j, smem, 0, Cfg::V_LOADS);
+                wait_vmcnt<0>();
+                barrier();
                 barrier();
             }
         } else {
@@ -407,13 +424,23 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void attn_kernel(const AttnArgs p)
             wait_vmcnt<(S - 2) * L>();
             barrier();
             int rs_ = 0;  // slot of tile j
-            for (int j = 0; j < nt; ++j) {
+            for (int j = 0; j < nt_w; ++j) {
                 const int cs = rs_ == 0 ? S - 1 : rs_ - 1;  // freed at the previous barrier
                 compute_tile(j, smem + rs_ * Cfg::SLOT_BYTES, j + S - 1, smem + cs * Cfg::SLOT_BYTES,
                              std::true_type());
                 // tile j+1 has landed once only the S-2 tiles issued after it
                 // may be in flight; after the barrier every wave is done with
                 // slot j and sees tile j+1
+                wait_vmcnt<(S - 2) * L>();
+                barrier();
+                rs_ = rs_ + 1 == S ? 0 : rs_ + 1;
+            }
+            // past this wave's diagonal: the same copies (K then V of tile
+            // j+S-1 into the slot the last barrier freed), waits and barriers
+            for (int j = nt_w; j < nt; ++j) {
+                const int cs = rs_ == 0 ? S - 1 : rs_ - 1;
+                issue_k(j + S - 1, smem + cs * Cfg::SLOT_BYTES, 0, Cfg::K_LOADS);
+                issue_v(j + S - 1, smem + cs * Cfg::SLOT_BYTES, 0, Cfg::V_LOADS);
                 wait_vmcnt<(S - 2) * L>();
                 barrier();
                 rs_ = rs_ + 1 == S ? 0 : rs_ + 1;
