@@ -72,6 +72,26 @@ int64_t attn_lds_bytes(int block_N, int dim, int num_stages);
 int attn_check(int64_t batch, int64_t heads, int64_t kv_heads, int64_t seq_q, int64_t seq_kv, int64_t dim, int dtype,
                int is_causal, int block_M, int block_N, int num_stages, int threads, int64_t lds_budget);
 
+/*
+ * attn_default_config: the gfx950 default configuration for these sizes
+ * (chapter 11, section 3.8: a tuned result fixed as the device's default),
+ * from timings of the built tiles at 4096 keys over 4 x 32 heads and on
+ * smaller grids:
+ *   - dim 128: block_M 256, block_N 128, 2 stages, 512 threads (8 waves);
+ *   - dim 64 without the mask: block_M 512, block_N 128, 2 stages, 512
+ *     threads (two 32-query blocks per wave);
+ *   - dim 64 with the mask, and wherever the 8-wave tile's grid
+ *     (batch x heads x ceil(seq_q / block_M)) would be under 256 workgroups,
+ *     one per compute unit: block_M 128, block_N 64, 2 stages, 256 threads
+ *     (4 waves; two such workgroups share a compute unit).
+ * Writes *block_M, *block_N, *num_stages and *threads.  Returns GEMM_OK,
+ * GEMM_ERR_ARG (a null output, a size below 1, is_causal not 0 or 1) or
+ * GEMM_ERR_UNSUPPORTED (a dim that is not built).  Pure host; the result
+ * passes attn_check for every size attn_fwd accepts.
+ */
+int attn_default_config(int64_t batch, int64_t heads, int64_t seq_q, int64_t dim, int is_causal, int *block_M,
+                        int *block_N, int *num_stages, int *threads);
+
 #ifdef __cplusplus
 }
 #endif

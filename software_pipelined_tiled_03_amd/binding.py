@@ -249,6 +249,9 @@ def _attn_lib():
         lib.attn_lds_bytes.restype = i64
         lib.attn_check.argtypes = [i64, i64, i64, i64, i64, i64, i32, i32, i32, i32, i32, i32, i64]
         lib.attn_check.restype = i32
+        ip = ctypes.POINTER(i32)
+        lib.attn_default_config.argtypes = [i64, i64, i64, i64, i32, ip, ip, ip, ip]
+        lib.attn_default_config.restype = i32
         _attn_declared = True
     return lib
 
@@ -271,10 +274,23 @@ def attn_check(batch, heads, kv_heads, seq_q, seq_kv, dim, dtype, is_causal, blo
                                       block_N, num_stages, threads, lds_budget))
 
 
-def attention(Q, K, V, causal=False, scale=0.0, out=None, block_M=128, block_N=64, num_stages=2, threads=0,
+def attn_default_config(batch, heads, seq_q, dim, is_causal):
+    """(block_M, block_N, num_stages, threads) of the gfx950 default table
+    for these sizes (attn_default_config in include/pipeattn.h)."""
+    out = [ctypes.c_int32() for _ in range(4)]
+    st = _attn_lib().attn_default_config(batch, heads, seq_q, dim, int(is_causal), *[ctypes.byref(x) for x in out])
+    _raise_for(st)
+    return tuple(x.value for x in out)
+
+
+def attention(Q, K, V, causal=False, scale=0.0, out=None, block_M=None, block_N=None, num_stages=None, threads=None,
               stream=None):
     """O = softmax(scale Q K^T [causal]) V on the GPU.  Q [B, H, Sq, D], K and V
-    [B, Hkv, Skv, D] contiguous fp16/bf16 device tensors; O like Q."""
+    [B, Hkv, Skv, D] contiguous fp16/bf16 device tensors; O like Q.  With
+    block_M left at None the tile comes from attn_default_config for these
+    sizes (block_N, num_stages and threads, if given, still apply); with
+    block_M given, the others default to 64 keys, 2 stages and one 32-query
+    block per wave."""
     import torch
     if Q.dim() != 4 or K.dim() != 4 or V.dim() != 4:
         raise GemmArgumentError(GEMM_ERR_ARG, "Q, K and V must be 4-D [batch, heads, seq, dim]")
@@ -290,6 +306,9 @@ def attention(Q, K, V, causal=False, scale=0.0, out=None, block_M=128, block_N=6
     if K.shape != V.shape or K.shape[0] != B or K.shape[3] != D:
         raise GemmArgumentError(GEMM_ERR_ARG, "K and V must be [batch, kv_heads, seq_kv, dim] matching Q")
     Hkv, Skv = K.shape[1], K.shape[2]
+    dflt = attn_default_config(B, H, Sq, D, causal) if block_M is None else (block_M, 64, 2, 0)
+    block_M, block_N, num_stages, threads = (d if v is None else v
+                                             for v, d in zip((block_M, block_N, num_stages, threads), dflt))
     if out is None:
         out = torch.empty_like(Q)
     elif out.shape != Q.shape or out.dtype != Q.dtype or not out.is_contiguous() or out.device != Q.device:

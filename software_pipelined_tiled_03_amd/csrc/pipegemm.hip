@@ -476,6 +476,36 @@ int64_t attn_lds_bytes(int block_N, int dim, int num_stages)
     return pipegemm::attn_lds_of(block_N, dim, num_stages);
 }
 
+int attn_default_config(int64_t batch, int64_t heads, int64_t seq_q, int64_t dim, int is_causal, int *block_M,
+                        int *block_N, int *num_stages, int *threads)
+{
+    using namespace pipegemm;
+    if (!block_M || !block_N || !num_stages || !threads)
+        return fail(GEMM_ERR_ARG, "block_M, block_N, num_stages and threads must not be null");
+    if (batch < 1 || heads < 1 || seq_q < 1)
+        return fail(GEMM_ERR_ARG, "attention sizes must be >= 1");
+    if (is_causal != 0 && is_causal != 1)
+        return fail(GEMM_ERR_ARG, "is_causal must be 0 or 1");
+    if (dim != 64 && dim != 128)
+        return fail(GEMM_ERR_UNSUPPORTED, "attention is built for dim 64 and 128 (got %lld)", (long long)dim);
+    // the 8-wave tiles, unless the grid would leave compute units idle
+    int bm = 256, bn = 128, s = 2, th = 512;
+    if (dim == 64)
+        bm = 512;
+    const int64_t nq = seq_q / bm + (seq_q % bm != 0);
+    const bool small = batch < 256 && heads < 256 && nq < 256 && batch * heads * nq < 256;
+    if ((dim == 64 && is_causal) || small) {
+        bm = 128;
+        bn = 64;
+        th = 256;
+    }
+    *block_M = bm;
+    *block_N = bn;
+    *num_stages = s;
+    *threads = th;
+    return ok();
+}
+
 int attn_check(int64_t batch, int64_t heads, int64_t kv_heads, int64_t seq_q, int64_t seq_kv, int64_t dim, int dtype,
                int is_causal, int block_M, int block_N, int num_stages, int threads, int64_t lds_budget)
 {

@@ -51,6 +51,16 @@ int main(void)
           "attention configuration");
     CHECK(attn_check(4, 32, 32, 4096, 4096, 128, GEMM_F16, 0, 256, 128, 3, 512, budget) == GEMM_ERR_LDS_BUDGET,
           "attention over budget");
+    {
+        int bm = 0, bn = 0, st = 0, th = 0;
+        CHECK(attn_default_config(4, 32, 4096, 128, 1, &bm, &bn, &st, &th) == GEMM_OK && bm == 256 && bn == 128 &&
+                  st == 2 && th == 512,
+              "attn_default_config");
+        CHECK(attn_check(4, 32, 32, 4096, 4096, 128, GEMM_F16, 1, bm, bn, st, th, budget) == GEMM_OK,
+              "attn_check of the default configuration");
+        CHECK(attn_default_config(1, 1, 1, 96, 0, &bm, &bn, &st, &th) == GEMM_ERR_UNSUPPORTED,
+              "attn_default_config rejects dim 96");
+    }
     printf("c consumer: OK (%d configurations; default %dx%dx%d S=%d lead=%d threads=%d)\n", n, d.block_M,
            d.block_N, d.block_K, d.num_stages, d.a_lead, d.threads);
     return 0;

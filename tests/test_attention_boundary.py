@@ -5,6 +5,8 @@ import ctypes
 import os
 import re
 
+import pytest
+
 from software_pipelined_tiled_03_amd import binding as pg
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -18,7 +20,7 @@ def declared():
 
 
 def test_header_and_exports():
-    assert declared() == ["attn_check", "attn_fwd", "attn_lds_bytes"]
+    assert declared() == ["attn_check", "attn_default_config", "attn_fwd", "attn_lds_bytes"]
     lib = ctypes.CDLL(pg.LIB_PATH)
     for name in declared():
         assert hasattr(lib, name), name
@@ -89,6 +91,37 @@ def test_sizes_past_the_limits_are_rejected_without_overflow():
     # workgroups: B H ceil(Sq / block_M) must stay below 2^31
     assert check(B=1 << 16, H=1 << 15, Hkv=1 << 15, Sq=128, Skv=64, bm=128) == pg.GEMM_ERR_UNSUPPORTED
     assert check(B=1 << 15, H=(1 << 16) - 1, Hkv=(1 << 16) - 1, Sq=128, Skv=64, bm=128) == pg.GEMM_OK
+
+
+def test_default_configuration_table():
+    D128, D64 = 128, 64
+    # the measured winners at 4096 keys over 4 x 32 heads
+    assert pg.attn_default_config(4, 32, 4096, D128, False) == (256, 128, 2, 512)
+    assert pg.attn_default_config(4, 32, 4096, D128, True) == (256, 128, 2, 512)
+    assert pg.attn_default_config(4, 32, 4096, D64, False) == (512, 128, 2, 512)
+    assert pg.attn_default_config(4, 32, 4096, D64, True) == (128, 64, 2, 256)
+    # a grid of fewer 8-wave workgroups than compute units takes the 4-wave tile
+    assert pg.attn_default_config(1, 16, 2048, D128, False) == (128, 64, 2, 256)   # 128 workgroups
+    assert pg.attn_default_config(1, 16, 4096, D128, False) == (256, 128, 2, 512)  # 256
+    assert pg.attn_default_config(2, 32, 2048, D64, False) == (512, 128, 2, 512)   # 256
+    assert pg.attn_default_config(1, 32, 2048, D64, False) == (128, 64, 2, 256)    # 128
+    # no overflow with huge sizes: plenty of workgroups
+    assert pg.attn_default_config(1 << 40, 1 << 40, 1 << 40, D128, False) == (256, 128, 2, 512)
+    # errors
+    with pytest.raises(pg.GemmArgumentError):
+        pg.attn_default_config(0, 1, 1, D128, False)
+    with pytest.raises(pg.UnsupportedConfigError):
+        pg.attn_default_config(1, 1, 1, 96, False)
+
+
+@pytest.mark.parametrize("B,H,Hkv,S,D,causal", [(4, 32, 32, 4096, 128, 0), (4, 32, 32, 4096, 64, 1),
+                                                 (1, 16, 16, 2048, 128, 1), (2, 32, 8, 300, 64, 0),
+                                                 (1, 1, 1, 1, 128, 1), (1, 4, 2, 8388600, 128, 0)])
+def test_default_configuration_passes_validation(B, H, Hkv, S, D, causal):
+    bm, bn, s, th = pg.attn_default_config(B, H, S, D, causal)
+    for dtype in (F16, BF16):
+        assert check(B=B, H=H, Hkv=Hkv, Sq=S, Skv=S, D=D, dtype=dtype, causal=causal, bm=bm, bn=bn, s=s,
+                     th=th) == pg.GEMM_OK, (bm, bn, s, th, pg.last_error())
 
 
 def test_scale_must_be_zero_or_positive_and_finite():

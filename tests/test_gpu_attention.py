@@ -221,3 +221,17 @@ def test_every_work_item_once(B, H, Hkv, causal):
                      num_stages=2, threads=th)
         torch.cuda.synchronize()
         assert_close(host(O), want, R, A, F16, 700, "B=%d H=%d Hkv=%d tile %d x %d" % (B, H, Hkv, bm, bn))
+
+
+@pytest.mark.parametrize("B,H,Hkv,S,D,causal", [(1, 4, 4, 600, 128, False), (2, 4, 2, 600, 128, True),
+                                                 (1, 4, 4, 600, 64, True), (1, 2, 2, 1100, 64, False)])
+def test_default_configuration(B, H, Hkv, S, D, causal):
+    # no tile arguments: the configuration comes from attn_default_config
+    w = inputs.attention_custom(F16, B, H, Hkv, S, S, D, causal, seed=1400 + S + D + causal)
+    Q, K, V = w.make()
+    want = oatt.attention(Q, K, V, F16, causal=causal)
+    R, A = weights(Q, K, V, F16, causal)
+    O = pg.attention(dev(Q, F16), dev(K, F16), dev(V, F16), causal=causal)
+    torch.cuda.synchronize()
+    assert_close(host(O), want, R, A, F16, S, "default configuration %s" % (pg.attn_default_config(B, H, S, D,
+                                                                                                     causal),))
