@@ -549,8 +549,12 @@ __global__ __launch_bounds__(Cfg::THREADS, 1) void gemm_kernel(const KernelArgs 
     // 0 for that k-step's first half, where it waits for the next tile; the
     // other wave of the SIMD, still in its MFMA stretch, then gets the issue
     // slots.  Measured on the 8-wave 256 x 256 tiles (4096^3, 84.7 -> 77.6 us
-    // with zero operands at 256 x 256 x 64); no gain on the 128 x 128 ones.
-    constexpr bool kPrio = Cfg::WAVES == 8 && Cfg::BM * Cfg::BN >= 256 * 256;
+    // with zero operands at 256 x 256 x 64), and with random operands on the
+    // 8-wave 128 x 256 x 64 tile: +1.5 % at S = 3 (NT), and +11 % (NT) and
+    // +15 % (NN) at S = 2 with a_lead, where it also brings the early B
+    // copies (ring_early_b); the 256 x 128 x 32 tile is unchanged.  No gain
+    // on the 128 x 128 ones.
+    constexpr bool kPrio = Cfg::WAVES == 8 && Cfg::BM * Cfg::BN >= 128 * 256;
     auto set_prio = [](auto level_c) __attribute__((always_inline)) {
         if constexpr (kPrio)
             __builtin_amdgcn_s_setprio(decltype(level_c)::value);
