@@ -100,9 +100,11 @@ ATTENTION = [
     ("attn_f16_b4_h32_s4096_d64", (512, 64, 512), (2, 3, 4)),
     ("attn_f16_b4_h32_s4096_d64", (512, 128, 512), (2,)),
     ("attn_f16_b4_h32_s4096_d64_causal", (512, 64, 512), (2, 3, 4)),
-    # 4 waves at D = 64
+    # 4 waves at D = 64, one and two 32-query blocks per wave
     ("attn_f16_b4_h32_s4096_d64", (128, 64, 256), (1, 2, 3)),
     ("attn_f16_b4_h32_s4096_d64_causal", (128, 64, 256), (1, 2, 3)),
+    ("attn_f16_b4_h32_s4096_d64", (256, 64, 256), (2, 3)),
+    ("attn_f16_b4_h32_s4096_d64_causal", (256, 64, 256), (2, 3)),
 ]
 PROFILES = os.path.join(ROOT, "profiles")
 
