@@ -26,7 +26,7 @@
  *    (the reference program: widen both operands to float, multiply with B
  *    transposed, cast back to the input dtype).
  *  - TileLang tutorial, code/04-tilelang-pipelined-gemm README, "expected
- *    output": correctness is judged against torch.matmul with fp16 inputs and
+ *    output": results are compared with torch.matmul with fp16 inputs and
  *    fp32 accumulation.
  *  - Tilelang-Learning notes "Stage 04 - GEMM", "concepts": the NN form
  *    C[M,N] = A[M,K] @ B[K,N] with fp32 accumulation for fp16/bf16 inputs.
