@@ -214,8 +214,13 @@ def stamp_summary(stamps, nk, flops=None, ms=None):
     workgroup id mod 8), the median prologue, K-loop and epilogue times, the
     K-loop cycles per K tile (median over workgroups), the workgroups resident
     per compute unit on average (summed workgroup time over the span times
-    256), and with `flops` and `ms` (the event time per launch) the MFMA
-    utilisation at the measured clock."""
+    256), and with `flops` the MFMA utilisation at the measured clock:
+    2MNK / time / (256 CUs x 4096 flop x clock), with the time taken from the
+    stamped launches themselves (`ms`, their event time per launch, or without
+    it the stamped launch's own span), never from other launches: the clock
+    under this load moves by 10 % and more between windows a few
+    milliseconds apart, so a clock from one window and a time from another
+    give a ratio that is off by as much."""
     import numpy as np
 
     s = stamps.view(-1, 6).cpu().numpy().astype(np.float64)
@@ -234,8 +239,9 @@ def stamp_summary(stamps, nk, flops=None, ms=None):
                loop_cycles_per_k_tile=round(float(np.median(s[:, 2] - s[:, 1])) / max(nk, 1), 1),
                wg_span_us=round(span_us, 3),
                wgs_resident_per_cu=round(float(rt.sum()) / 100.0 / (span_us * CUS), 2) if span_us > 0 else None)
-    if flops is not None and ms:
-        out["mfma_util_at_clock"] = round(flops / (ms * 1e-3) / (CUS * 4096 * clock * 1e9), 4)
+    t_ms = ms if ms else (span_us * 1e-3 if span_us > 0 else None)
+    if flops is not None and t_ms:
+        out["mfma_util_at_clock"] = round(flops / (t_ms * 1e-3) / (CUS * 4096 * clock * 1e9), 4)
     return out
 
 
@@ -550,7 +556,7 @@ def main():
                 # one more launch with clock stamps: clock, phases, cycles per K tile
                 _, stamps = pg.gemm_stamped(pg.GEMM_NT if lay == "nt" else pg.GEMM_NN, sA, sB, out=sC, block=block,
                                             num_stages=s, threads=th, a_lead=lead)
-                st = stamp_summary(stamps, -(-sK // block[2]), sflops, ms)
+                st = stamp_summary(stamps, -(-sK // block[2]), sflops)
                 lds = pg.gemm_lds_bytes(block[0], block[1], block[2], s, a_lead=lead)
                 row[d] = dict(tflops=round(sflops / ms / 1e9, 1),
                               pct_peak=round(100 * sflops / ms / 1e9 / PEAK_TFLOPS, 1),
@@ -616,9 +622,8 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         sms = e0.elapsed_time(e1) / reps
-        # utilisation against the timed launches' own time, at the clock the
-        # launches right after them ran at
-        clock = stamp_summary(stamps, -(-w.K // block[2]), flops, ms)
+        # utilisation of these stamped launches: their clock and their own time
+        clock = stamp_summary(stamps, -(-w.K // block[2]), flops, sms)
         clock["launches"] = reps
         clock["ms_per_launch"] = round(sms, 5)
         _log("clock %.3f GHz (XCDs %s), MFMA utilisation at that clock %.3f; prologue %.2f us, loop %.2f us, "

@@ -139,3 +139,9 @@ def test_stamp_summary_reduces_clock_phases_and_residency():
     assert st["prologue_us"] == pytest.approx(0.5, abs=1e-3)      # 1000 cycles at 2 GHz (median)
     # 16 workgroups on 256 compute units: 1/16 resident per CU on average over the span
     assert st["wgs_resident_per_cu"] == pytest.approx(16 / 256 * (14 * 33.5 + 2 * 44.667) / 16 / 44.667, abs=0.01)
+    # utilisation: the stamped launches' own time (ms), else the launch's own
+    # span (44.667 us here), at the mean clock (14 x 2.0 + 2 x 1.5) / 16 GHz
+    flops, clock = 2.0 * 256 * 4096 * 67000, (14 * 2.0 + 2 * 1.5) / 16
+    assert st["mfma_util_at_clock"] == pytest.approx(flops / 33.5e-6 / (256 * 4096 * clock * 1e9), rel=1e-3)
+    st = bench.stamp_summary(torch.tensor(rows, dtype=torch.float64).to(torch.int64), 64, flops=flops)
+    assert st["mfma_util_at_clock"] == pytest.approx(flops / 44.667e-6 / (256 * 4096 * clock * 1e9), rel=1e-3)
