@@ -17,7 +17,7 @@ per ring depth on its workloads and reported under "attention".
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-sweep] [--no-cpu-baseline]
                        [--no-attention | --attention] [--no-clock] [--workload W --block BMxBNxBK
-                       --stages S[+A] --threads T] [--tune-tables] [--oracle-table]
+                       --stages S[+A] --threads T] [--tune-tables] [--oracle-table] [--sustain SECONDS]
 """
 import argparse
 import json
@@ -467,6 +467,32 @@ def oracle_table():
     return 0
 
 
+def sustain(fn, dA, dB, C, flops, seconds):
+    """The headline configuration launched back to back for `seconds`
+    windows of about one second each (HIP events around each; the first, of
+    100 launches, sizes the others), one JSON line per window."""
+    import torch
+
+    block, stages, a_lead, threads = HEADLINE["block"], HEADLINE["num_stages"], HEADLINE["a_lead"], HEADLINE["threads"]
+    per_window = None
+    for sec in range(seconds):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = per_window or 100
+        t0 = time.time()
+        e0.record()
+        for _ in range(n):
+            fn(dA, dB, out=C, block=block, num_stages=stages, threads=threads, a_lead=a_lead)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        if per_window is None:
+            # size the windows to about one second from the first short one
+            per_window = max(100, int(1000.0 / ms))
+        print(json.dumps({"sustain_s": sec, "launches": n, "ms_per_launch": round(ms, 5),
+                          "tflops": round(flops / ms / 1e9, 1), "wall_s": round(time.time() - t0, 3)}), flush=True)
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -491,6 +517,10 @@ def main():
     ap.add_argument("--oracle-table-worker", type=int, default=None, help=argparse.SUPPRESS)
     ap.add_argument("--tune-tables", action="store_true",
                     help="only measure every built configuration on the tuning shapes (one JSON line per shape)")
+    ap.add_argument("--sustain", type=int, default=0,
+                    help="only run the headline configuration back to back for this many windows of about a second "
+                         "(at most 120), one JSON line per window: a steady load for reading board power and clocks "
+                         "beside it")
     args = ap.parse_args()
 
     if args.oracle_table_worker is not None:
@@ -532,6 +562,9 @@ def main():
     fn = pg.gemm_nt if w.layout == "nt" else pg.gemm_nn
     C = torch.empty((w.M, w.N), dtype=dA.dtype, device="cuda")
     flops = 2.0 * w.M * w.N * w.K
+
+    if args.sustain:
+        return sustain(fn, dA, dB, C, flops, min(args.sustain, 120))
 
     sweep = {}
     if not args.no_sweep:
