@@ -467,13 +467,12 @@ def oracle_table():
     return 0
 
 
-def sustain(fn, dA, dB, C, flops, seconds):
-    """The headline configuration launched back to back for `seconds`
-    windows of about one second each (HIP events around each; the first, of
-    100 launches, sizes the others), one JSON line per window."""
+def sustain(call, flops, seconds):
+    """`call` (one launch) back to back for `seconds` windows of about one
+    second each (HIP events around each; the first, of 100 launches, sizes
+    the others), one JSON line per window."""
     import torch
 
-    block, stages, a_lead, threads = HEADLINE["block"], HEADLINE["num_stages"], HEADLINE["a_lead"], HEADLINE["threads"]
     per_window = None
     for sec in range(seconds):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -481,12 +480,11 @@ def sustain(fn, dA, dB, C, flops, seconds):
         t0 = time.time()
         e0.record()
         for _ in range(n):
-            fn(dA, dB, out=C, block=block, num_stages=stages, threads=threads, a_lead=a_lead)
+            call()
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / n
         if per_window is None:
-            # size the windows to about one second from the first short one
             per_window = max(100, int(1000.0 / ms))
         print(json.dumps({"sustain_s": sec, "launches": n, "ms_per_launch": round(ms, 5),
                           "tflops": round(flops / ms / 1e9, 1), "wall_s": round(time.time() - t0, 3)}), flush=True)
@@ -518,9 +516,10 @@ def main():
     ap.add_argument("--tune-tables", action="store_true",
                     help="only measure every built configuration on the tuning shapes (one JSON line per shape)")
     ap.add_argument("--sustain", type=int, default=0,
-                    help="only run the headline configuration back to back for this many windows of about a second "
-                         "(at most 120), one JSON line per window: a steady load for reading board power and clocks "
-                         "beside it")
+                    help="only run the headline configuration (with --attention: the attention forward pass of the "
+                         "first attention workload, default tile) back to back for this many windows of about a "
+                         "second (at most 120), one JSON line per window: a steady load for reading board power "
+                         "and clocks beside it")
     args = ap.parse_args()
 
     if args.oracle_table_worker is not None:
@@ -557,6 +556,14 @@ def main():
         print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "launches": 5}))
         return 0
 
+    if args.sustain and args.attention:
+        import numpy as np
+        aw = inputs.attention_workload(ATTENTION[0][0])
+        dQ, dK, dV = [torch.from_numpy(x.view(np.int16)).cuda().view(torch.float16) for x in aw.make()]
+        O = torch.empty_like(dQ)
+        # the default tile for these sizes (attn_default_config)
+        return sustain(lambda: pg.attention(dQ, dK, dV, causal=aw.causal, out=O), aw.flops, min(args.sustain, 120))
+
     w = inputs.workload(args.workload)
     A, B, dA, dB = _device_inputs(w)
     fn = pg.gemm_nt if w.layout == "nt" else pg.gemm_nn
@@ -564,7 +571,9 @@ def main():
     flops = 2.0 * w.M * w.N * w.K
 
     if args.sustain:
-        return sustain(fn, dA, dB, C, flops, min(args.sustain, 120))
+        hb, hs, hl, ht = HEADLINE["block"], HEADLINE["num_stages"], HEADLINE["a_lead"], HEADLINE["threads"]
+        return sustain(lambda: fn(dA, dB, out=C, block=hb, num_stages=hs, threads=ht, a_lead=hl), flops,
+                       min(args.sustain, 120))
 
     sweep = {}
     if not args.no_sweep:
